@@ -131,7 +131,7 @@ class Inputs:
     """
 
     def __init__(self, wl: Workload, experts: bool = True, dy: Optional[bool] = None,
-                 N: Optional[int] = None):
+                 N: Optional[int] = None, progress=None):
         self.wl = wl
         self.N = wl.N if N is None else N
         s = wl.seed
@@ -151,6 +151,8 @@ class Inputs:
             for e in range(wl.E):
                 g, u, d = self.expert_storage(e)
                 self.Wg[e], self.Wu[e], self.Wd[e] = g, u, d
+                if progress is not None and (e + 1) % 16 == 0:
+                    progress(f"{wl.name}: experts {e + 1}/{wl.E} drawn")
 
     def expert_storage(self, e: int):
         wl = self.wl

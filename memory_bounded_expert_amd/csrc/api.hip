@@ -1,0 +1,346 @@
+// C ABI of libmoebound: argument checks, the eq. (1) chunk plan, workspace
+// carving and the per-chunk launch sequence.
+//
+// The chunk schedule follows the "Bounded-streaming operators" summary,
+// Methodology 1 (PipelinedLLEP): eq. (1) gives K and c_eff, chunk i holds the
+// strided token positions i, i+K, ..., and the dispatch buffers are sized by
+// k * c_eff rows, never by N ("Memory bound", read with E_p = 1 and c_eff).
+// The backward pass recomputes each chunk's expert intermediates from X and
+// reuses the same buffers for the next chunk ("Nested gradient
+// checkpointing"; hop-local recomputation in "Memory-Efficient Expert Routing
+// for Distributed MoE Training", section 3.3).
+//
+// The library allocates nothing and never synchronises: every buffer comes
+// from the caller's workspace and every kernel goes on the caller's stream.
+#include <algorithm>
+#include <cstring>
+
+#include "moe_internal.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace moe {
+
+Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_dgates) {
+  Layout L;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = cur;
+    cur = (cur + bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t N = (size_t)p.N, k = (size_t)p.k, E = (size_t)p.E, H = (size_t)p.H,
+               F = (size_t)p.F, K = (size_t)p.K, ce = (size_t)p.c_eff;
+  const size_t b = (size_t)elem_bytes(p.dtype);
+  if (N == 0) return L;
+  L.nblk = ceil_div((int64_t)ce, kPlanBlock);
+  L.max_tiles = max_row_tiles((int64_t)(k * ce), (int)E);
+  if (pass == Pass::Forward && need_logits) L.logits = take(N * E * 4);
+  L.rank = take(N * k * 4);
+  L.blk = take(K * (size_t)L.nblk * E * 4);
+  L.offsets = take(K * (E + 1) * 4);
+  L.tiles = take(K * (size_t)L.max_tiles * 8);
+  L.tile_count = take(K * 4);
+  if (pass != Pass::Debug) {
+    L.perm = take(N * k * 4);
+    L.pos = take(N * k * 4);
+    const size_t rows = k * ce;
+    L.xp = take(rows * H * b);
+    L.o = take(rows * H * b);
+    L.h = take(rows * F * b);
+    if (pass == Pass::Backward) {
+      L.a = take(rows * F * b);
+      L.u = take(rows * F * b);
+      L.dh = take(rows * F * 4);
+      L.wrt = take(E * H * b);
+      if (need_dgates) L.dgates = take(N * k * 4);
+    }
+  }
+  L.total = cur;
+  return L;
+}
+
+namespace {
+
+bool plan_ok(const moe_plan_t* p) { return p != nullptr && p->magic == kPlanMagic; }
+
+PlanBuffers plan_buffers(char* ws, const Layout& L, int32_t* offsets, int32_t* perm,
+                         int32_t* pos) {
+  PlanBuffers b;
+  b.rank = (int32_t*)(ws + L.rank);
+  b.blk = (int32_t*)(ws + L.blk);
+  b.offsets = offsets ? offsets : (int32_t*)(ws + L.offsets);
+  b.tiles = (int2*)(ws + L.tiles);
+  b.tile_count = (int32_t*)(ws + L.tile_count);
+  b.perm = perm ? perm : (int32_t*)(ws + L.perm);
+  b.pos = pos ? pos : (int32_t*)(ws + L.pos);
+  b.nblk = L.nblk;
+  b.max_tiles = L.max_tiles;
+  return b;
+}
+
+RowsGeom rows_geom(const PlanBuffers& b, const moe_plan_t& P, int i, int64_t R) {
+  RowsGeom g;
+  g.tiles = b.tiles + (int64_t)i * b.max_tiles;
+  g.tile_count = b.tile_count + i;
+  g.offsets = b.offsets + (int64_t)i * (P.E + 1);
+  g.grid_m = max_row_tiles(R, P.E);
+  return g;
+}
+
+void fill_stats(moe_stats_t* s, const moe_plan_t& P, int launches, size_t ws, size_t inter) {
+  if (!s) return;
+  std::memset(s, 0, sizeof(*s));
+  s->K = P.K;
+  s->launches = launches;
+  s->c_eff = P.c_eff;
+  s->max_pairs_per_chunk = (int64_t)P.k * P.c_eff;  // chunk 0 holds c_eff tokens
+  s->dispatch_bytes = 2 * (int64_t)P.k * P.c_eff * P.H * elem_bytes(P.dtype);
+  s->dispatch_bound_bytes = P.dispatch_bound_bytes;
+  s->intermediate_bytes = (int64_t)inter;
+  s->workspace_bytes = (int64_t)ws;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+#define MOE_CHECK(call)                        \
+  do {                                         \
+    if ((call) != hipSuccess) return MOE_EHIP; \
+    ++launches;                                \
+  } while (0)
+
+MOE_API const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP runtime error at enqueue";
+    default: return "unknown status";
+  }
+}
+
+MOE_API int moe_plan_chunks(int64_t N, int32_t H, int32_t F, int32_t E, int32_t k, int32_t c,
+                            int32_t K_max, int32_t dtype, moe_plan_t* out) {
+  if (!out || N < 0 || c < 1 || K_max < 1 || k < 1 || H < 1 || F < 1 || E < 1 || k > E)
+    return MOE_EINVAL;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EINVAL;
+  const int epc = dtype == MOE_BF16 ? 8 : 4;
+  if (H % 64 || F % 64 || E % epc || E > 1024 || k > 64) return MOE_EUNSUPPORTED;
+  if (N * (int64_t)k >= ((int64_t)1 << 31)) return MOE_EUNSUPPORTED;
+  moe_plan_t p;
+  std::memset(&p, 0, sizeof(p));
+  p.magic = kPlanMagic;
+  p.dtype = dtype;
+  p.N = N;
+  p.H = H;
+  p.F = F;
+  p.E = E;
+  p.k = k;
+  p.c = c;
+  p.K_max = K_max;
+  if (N > 0) {
+    const int64_t K = std::min<int64_t>(ceil_div(N, c), K_max);  // eq. (1)
+    if (K > 65535) return MOE_EUNSUPPORTED;
+    p.K = (int32_t)K;
+    p.c_eff = ceil_div(N, K);  // eq. (1)
+  }
+  p.max_pairs_per_chunk = (int64_t)k * p.c_eff;
+  p.dispatch_bound_bytes = 2 * (int64_t)k * p.c_eff * H * elem_bytes(dtype);
+  p.fwd_workspace_bytes = (int64_t)make_layout(p, Pass::Forward, true, false).total;
+  p.bwd_workspace_bytes = (int64_t)make_layout(p, Pass::Backward, false, true).total;
+  p.debug_workspace_bytes = (int64_t)make_layout(p, Pass::Debug, false, false).total;
+  *out = p;
+  return MOE_OK;
+}
+
+MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const void* W_r,
+                                const float* router_bias, const void* W_gate, const void* W_up,
+                                const void* W_down, void* Y, int32_t* topk_idx, float* gates,
+                                float* logits, void* workspace, size_t workspace_bytes,
+                                void* stream, moe_stats_t* stats) {
+  if (!plan_ok(plan)) return MOE_EINVAL;
+  const moe_plan_t& P = *plan;
+  if (P.N == 0) {
+    fill_stats(stats, P, 0, 0, 0);
+    return MOE_OK;
+  }
+  if (!X || !W_r || !W_gate || !W_up || !W_down || !Y || !topk_idx || !gates || !workspace)
+    return MOE_EINVAL;
+  if ((uintptr_t)workspace % 256) return MOE_EINVAL;
+  if (workspace_bytes < (size_t)P.fwd_workspace_bytes) return MOE_EWORKSPACE;
+  const Layout L = make_layout(P, Pass::Forward, logits == nullptr, false);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* lg = logits ? logits : (float*)(ws + L.logits);
+  int launches = 0;
+  (void)hipGetLastError();
+
+  MOE_CHECK(gemm_router(P.dtype, X, W_r, router_bias, lg, P.N, P.H, P.E, st));
+  MOE_CHECK(launch_topk(lg, P.N, P.E, P.k, topk_idx, gates, st));
+  const PlanBuffers pb = plan_buffers(ws, L, nullptr, nullptr, nullptr);
+  MOE_CHECK(launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st));
+  launches += 2;
+  void* xp = ws + L.xp;
+  void* o = ws + L.o;
+  void* h = ws + L.h;
+  for (int i = 0; i < P.K; ++i) {
+    const ChunkGeom g = chunk_geom(P.N, P.K, P.k, i);
+    const int64_t R = (int64_t)P.k * g.n;
+    const RowsGeom rg = rows_geom(pb, P, i, R);
+    const int32_t* perm_i = pb.perm + g.pair_base;
+    MOE_CHECK(launch_gather(P.dtype, X, xp, perm_i, R, P.k, P.N, P.H, st));
+    MOE_CHECK(gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st));
+    MOE_CHECK(gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st));
+    MOE_CHECK(launch_combine(P.dtype, o, pb.pos, gates, Y, P.N, P.K, i, g.n, P.k, P.H, st));
+  }
+  fill_stats(stats, P, launches, L.total,
+             (size_t)P.k * P.c_eff * P.F * elem_bytes(P.dtype));
+  return MOE_OK;
+}
+
+MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const void* W_r,
+                                 const void* W_gate, const void* W_up, const void* W_down,
+                                 const void* dY, const int32_t* topk_idx, const float* gates,
+                                 void* dX, float* dW_gate, float* dW_up, float* dW_down,
+                                 float* dlogits, float* dgates, float* dW_r, void* workspace,
+                                 size_t workspace_bytes, void* stream, moe_stats_t* stats) {
+  if (!plan_ok(plan)) return MOE_EINVAL;
+  const moe_plan_t& P = *plan;
+  if (!dW_gate || !dW_up || !dW_down) return MOE_EINVAL;
+  if (P.N > 0 && (!X || !W_r || !W_gate || !W_up || !W_down || !dY || !topk_idx || !gates ||
+                  !dX || !dlogits || !workspace))
+    return MOE_EINVAL;
+  if (P.N > 0 && (uintptr_t)workspace % 256) return MOE_EINVAL;
+  if (workspace_bytes < (size_t)P.bwd_workspace_bytes) return MOE_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int launches = 0;
+  (void)hipGetLastError();
+  const size_t wbytes = (size_t)P.E * P.H * P.F * sizeof(float);
+  MOE_CHECK(launch_fill_zero(dW_gate, wbytes, st));
+  MOE_CHECK(launch_fill_zero(dW_up, wbytes, st));
+  MOE_CHECK(launch_fill_zero(dW_down, wbytes, st));
+  if (dW_r) MOE_CHECK(launch_fill_zero(dW_r, (size_t)P.H * P.E * sizeof(float), st));
+  if (P.N == 0) {
+    fill_stats(stats, P, launches, 0, 0);
+    return MOE_OK;
+  }
+  const Layout L = make_layout(P, Pass::Backward, false, dgates == nullptr);
+  char* ws = (char*)workspace;
+  float* dg = dgates ? dgates : (float*)(ws + L.dgates);
+  void* wrt = ws + L.wrt;
+  MOE_CHECK(launch_transpose(P.dtype, W_r, wrt, P.H, P.E, st));
+  const PlanBuffers pb = plan_buffers(ws, L, nullptr, nullptr, nullptr);
+  MOE_CHECK(launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st));
+  launches += 2;
+  void* xp = ws + L.xp;
+  void* o = ws + L.o;  // dY rows, then dXp
+  void* h = ws + L.h;  // h, then g h
+  void* a = ws + L.a;  // a, then da
+  void* u = ws + L.u;  // u, then du
+  float* dh = (float*)(ws + L.dh);
+  for (int i = 0; i < P.K; ++i) {
+    const ChunkGeom g = chunk_geom(P.N, P.K, P.k, i);
+    const int64_t R = (int64_t)P.k * g.n;
+    const RowsGeom rg = rows_geom(pb, P, i, R);
+    const int32_t* perm_i = pb.perm + g.pair_base;
+    // recompute this chunk's expert intermediates
+    MOE_CHECK(launch_gather(P.dtype, X, xp, perm_i, R, P.k, P.N, P.H, st));
+    MOE_CHECK(gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, a, u, P.H, P.F, st));
+    // backward through the chunk
+    MOE_CHECK(launch_gather(P.dtype, dY, o, perm_i, R, P.k, P.N, P.H, st));
+    MOE_CHECK(gemm_dh(P.dtype, rg, o, W_down, dh, P.H, P.F, st));
+    MOE_CHECK(launch_swiglu_bwd(P.dtype, dh, a, u, h, perm_i, gates, dg, R, P.F, P.N * P.k, st));
+    MOE_CHECK(gemm_wgrad_d(P.dtype, rg.offsets, h, o, dW_down, P.E, P.H, P.F, st));
+    MOE_CHECK(gemm_wgrad_gu(P.dtype, rg.offsets, xp, a, u, dW_gate, dW_up, P.E, P.H, P.F, st));
+    MOE_CHECK(gemm_dx(P.dtype, rg, a, u, W_gate, W_up, o, P.H, P.F, st));
+    MOE_CHECK(launch_combine_bwd(P.dtype, o, wrt, topk_idx, pb.pos, gates, dg, dX, dlogits, P.N,
+                                 P.K, i, g.n, P.k, P.E, P.H, st));
+    if (dW_r)
+      MOE_CHECK(launch_dwr(P.dtype, xp, perm_i, rg.offsets, dlogits, dW_r, P.k, P.E, P.H, P.N, st));
+  }
+  fill_stats(stats, P, launches, L.total,
+             (size_t)P.k * P.c_eff * P.F * (3 * elem_bytes(P.dtype) + 4));
+  return MOE_OK;
+}
+
+MOE_API int moe_debug_topk(const float* logits, int64_t N, int32_t E, int32_t k,
+                           int32_t* topk_idx, float* gates, void* stream) {
+  if (N < 0 || k < 1 || E < 1 || k > E) return MOE_EINVAL;
+  if (E > 1024 || k > 64) return MOE_EUNSUPPORTED;
+  if (N == 0) return MOE_OK;
+  if (!logits || !topk_idx || !gates) return MOE_EINVAL;
+  (void)hipGetLastError();
+  return launch_topk(logits, N, E, k, topk_idx, gates, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_EHIP;
+}
+
+MOE_API int moe_debug_plan(const moe_plan_t* plan, const int32_t* topk_idx, int32_t* offsets,
+                           int32_t* perm, int32_t* pos, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!plan_ok(plan)) return MOE_EINVAL;
+  const moe_plan_t& P = *plan;
+  if (P.N == 0) return MOE_OK;
+  if (!topk_idx || !offsets || !perm || !pos || !workspace) return MOE_EINVAL;
+  if ((uintptr_t)workspace % 256) return MOE_EINVAL;
+  if (workspace_bytes < (size_t)P.debug_workspace_bytes) return MOE_EWORKSPACE;
+  const Layout L = make_layout(P, Pass::Debug, false, false);
+  (void)hipGetLastError();
+  const PlanBuffers pb = plan_buffers((char*)workspace, L, offsets, perm, pos);
+  return launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_EHIP;
+}
+
+MOE_API int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk, const void* X,
+                            const void* W_r, const float* router_bias, const void* W_gate,
+                            const void* W_up, const void* W_down, void* Y, int32_t* topk_idx,
+                            float* gates, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan_ok(plan)) return MOE_EINVAL;
+  const moe_plan_t& P = *plan;
+  if (P.N == 0 || stage < MOE_STAGE_ROUTER || stage > MOE_STAGE_COMBINE) return MOE_EINVAL;
+  if (stage >= MOE_STAGE_GATHER && (chunk < 0 || chunk >= P.K)) return MOE_EINVAL;
+  if (!X || !W_r || !W_gate || !W_up || !W_down || !Y || !topk_idx || !gates || !workspace)
+    return MOE_EINVAL;
+  if ((uintptr_t)workspace % 256) return MOE_EINVAL;
+  if (workspace_bytes < (size_t)P.fwd_workspace_bytes) return MOE_EWORKSPACE;
+  const Layout L = make_layout(P, Pass::Forward, true, false);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* lg = (float*)(ws + L.logits);
+  const PlanBuffers pb = plan_buffers(ws, L, nullptr, nullptr, nullptr);
+  (void)hipGetLastError();
+  hipError_t err = hipSuccess;
+  if (stage == MOE_STAGE_ROUTER) {
+    err = gemm_router(P.dtype, X, W_r, router_bias, lg, P.N, P.H, P.E, st);
+  } else if (stage == MOE_STAGE_TOPK) {
+    err = launch_topk(lg, P.N, P.E, P.k, topk_idx, gates, st);
+  } else if (stage == MOE_STAGE_PLAN) {
+    err = launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st);
+  } else {
+    const ChunkGeom g = chunk_geom(P.N, P.K, P.k, chunk);
+    const int64_t R = (int64_t)P.k * g.n;
+    const RowsGeom rg = rows_geom(pb, P, chunk, R);
+    void* xp = ws + L.xp;
+    void* o = ws + L.o;
+    void* h = ws + L.h;
+    switch (stage) {
+      case MOE_STAGE_GATHER:
+        err = launch_gather(P.dtype, X, xp, pb.perm + g.pair_base, R, P.k, P.N, P.H, st);
+        break;
+      case MOE_STAGE_GEMM_UP:
+        err = gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st);
+        break;
+      case MOE_STAGE_GEMM_DOWN:
+        err = gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st);
+        break;
+      default:
+        err = launch_combine(P.dtype, o, pb.pos, gates, Y, P.N, P.K, chunk, g.n, P.k, P.H, st);
+    }
+  }
+  return err == hipSuccess ? MOE_OK : MOE_EHIP;
+}

@@ -1,0 +1,98 @@
+// Backward contractions: dY W_down^T, [da du] [W_gate W_up]^T, and the
+// per-expert weight gradients accumulated chunk by chunk.
+#include "gemm_kernel.hpp"
+
+namespace moe {
+using namespace gemm;
+
+namespace {
+template <typename T>
+hipError_t dh_t(const Params& p, dim3 grid, int bn, hipStream_t st) {
+  if (bn == 256) return launch<T, Mode::Rows, 128, 256, false, true, true, false, Epi::F32>(p, grid, st);
+  if (bn == 128) return launch<T, Mode::Rows, 128, 128, false, true, true, false, Epi::F32>(p, grid, st);
+  return launch<T, Mode::Rows, 128, 64, false, true, true, false, Epi::F32>(p, grid, st);
+}
+
+template <typename T>
+hipError_t dx_t(const Params& p, dim3 grid, int bn, hipStream_t st) {
+  if (bn == 256) return launch<T, Mode::Rows, 128, 256, false, true, true, true, Epi::Store>(p, grid, st);
+  if (bn == 128) return launch<T, Mode::Rows, 128, 128, false, true, true, true, Epi::Store>(p, grid, st);
+  return launch<T, Mode::Rows, 128, 64, false, true, true, true, Epi::Store>(p, grid, st);
+}
+
+template <typename T, int BM>
+hipError_t wgu_t(const Params& p, dim3 grid, int bn, hipStream_t st) {
+  if (bn == 128) return launch<T, Mode::Expert, BM, 128, true, false, false, false, Epi::AccF32>(p, grid, st);
+  return launch<T, Mode::Expert, BM, 64, true, false, false, false, Epi::AccF32>(p, grid, st);
+}
+
+template <typename T, int BM>
+hipError_t wd_t(const Params& p, dim3 grid, int bn, hipStream_t st) {
+  if (bn == 256) return launch<T, Mode::Expert, BM, 256, false, false, false, false, Epi::AccF32>(p, grid, st);
+  if (bn == 128) return launch<T, Mode::Expert, BM, 128, false, false, false, false, Epi::AccF32>(p, grid, st);
+  return launch<T, Mode::Expert, BM, 64, false, false, false, false, Epi::AccF32>(p, grid, st);
+}
+}  // namespace
+
+hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd, float* dh, int H,
+                   int F, hipStream_t st) {
+  if (g.grid_m == 0) return hipSuccess;
+  Params p{};
+  p.A = dYp; p.lda = H;
+  p.B = Wd; p.ldb = H; p.b_estride = (int64_t)F * H;  // row f of W_down[e] holds K = H
+  p.C = dh; p.ldc = F;
+  p.N = F; p.K = H;
+  p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
+  const int bn = pick_bn(F, true);
+  const dim3 grid((unsigned)g.grid_m, (unsigned)(F / bn));
+  return dtype == MOE_BF16 ? dh_t<bf16_t>(p, grid, bn, st) : dh_t<float>(p, grid, bn, st);
+}
+
+hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du, const void* Wg,
+                   const void* Wu, void* dXp, int H, int F, hipStream_t st) {
+  if (g.grid_m == 0) return hipSuccess;
+  Params p{};
+  p.A = da; p.A2 = du; p.lda = F;
+  p.B = Wg; p.B2 = Wu; p.ldb = F; p.b_estride = (int64_t)H * F;  // row h of W_gate[e] holds K = F
+  p.C = dXp; p.ldc = H;
+  p.N = H; p.K = 2 * F; p.Kseg = F;
+  p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
+  const int bn = pick_bn(H, true);
+  const dim3 grid((unsigned)g.grid_m, (unsigned)(H / bn));
+  return dtype == MOE_BF16 ? dx_t<bf16_t>(p, grid, bn, st) : dx_t<float>(p, grid, bn, st);
+}
+
+hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, const void* da,
+                         const void* du, float* dWg, float* dWu, int E, int H, int F,
+                         hipStream_t st) {
+  Params p{};
+  p.A = Xp; p.lda = H;
+  p.B = da; p.B2 = du; p.ldb = F;
+  p.C = dWg; p.C2 = dWu; p.ldc = F; p.c_estride = (int64_t)H * F;
+  p.M = H; p.N = F;
+  p.offsets = offsets;
+  const int bm = H % 128 == 0 ? 128 : 64;
+  const int bn = F % 128 == 0 ? 128 : 64;
+  const dim3 grid((unsigned)(H / bm), (unsigned)(F / bn), (unsigned)E);
+  if (dtype == MOE_BF16)
+    return bm == 128 ? wgu_t<bf16_t, 128>(p, grid, bn, st) : wgu_t<bf16_t, 64>(p, grid, bn, st);
+  return bm == 128 ? wgu_t<float, 128>(p, grid, bn, st) : wgu_t<float, 64>(p, grid, bn, st);
+}
+
+hipError_t gemm_wgrad_d(int dtype, const int32_t* offsets, const void* hg, const void* dYp,
+                        float* dWd, int E, int H, int F, hipStream_t st) {
+  Params p{};
+  p.A = hg; p.lda = F;
+  p.B = dYp; p.ldb = H;
+  p.C = dWd; p.ldc = H; p.c_estride = (int64_t)F * H;
+  p.M = F; p.N = H;
+  p.offsets = offsets;
+  const int bm = F % 128 == 0 ? 128 : 64;
+  const int bn = pick_bn(H, true);
+  const dim3 grid((unsigned)(F / bm), (unsigned)(H / bn), (unsigned)E);
+  if (dtype == MOE_BF16)
+    return bm == 128 ? wd_t<bf16_t, 128>(p, grid, bn, st) : wd_t<bf16_t, 64>(p, grid, bn, st);
+  return bm == 128 ? wd_t<float, 128>(p, grid, bn, st) : wd_t<float, 64>(p, grid, bn, st);
+}
+
+}  // namespace moe

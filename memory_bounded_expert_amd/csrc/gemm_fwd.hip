@@ -1,0 +1,72 @@
+// Forward contractions: router logits, expert up-projection with the fused
+// SwiGLU epilogue, expert down-projection.
+#include "gemm_kernel.hpp"
+
+namespace moe {
+using namespace gemm;
+
+namespace {
+template <typename T>
+hipError_t up_swiglu_t(const Params& p, dim3 grid, int bn, bool save, hipStream_t st) {
+  if (bn == 128) {
+    return save ? launch<T, Mode::Rows, 128, 128, true, true, false, false, Epi::SwiGLUSave>(p, grid, st)
+                : launch<T, Mode::Rows, 128, 128, true, true, false, false, Epi::SwiGLU>(p, grid, st);
+  }
+  return save ? launch<T, Mode::Rows, 128, 64, true, true, false, false, Epi::SwiGLUSave>(p, grid, st)
+              : launch<T, Mode::Rows, 128, 64, true, true, false, false, Epi::SwiGLU>(p, grid, st);
+}
+
+template <typename T>
+hipError_t down_t(const Params& p, dim3 grid, int bn, hipStream_t st) {
+  if (bn == 256) return launch<T, Mode::Rows, 128, 256, false, true, false, false, Epi::Store>(p, grid, st);
+  if (bn == 128) return launch<T, Mode::Rows, 128, 128, false, true, false, false, Epi::Store>(p, grid, st);
+  return launch<T, Mode::Rows, 128, 64, false, true, false, false, Epi::Store>(p, grid, st);
+}
+}  // namespace
+
+hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const void* Wg,
+                          const void* Wu, void* h, void* a, void* u, int H, int F, hipStream_t st) {
+  if (g.grid_m == 0) return hipSuccess;
+  Params p{};
+  p.A = Xp; p.lda = H;
+  p.B = Wg; p.B2 = Wu; p.ldb = F; p.b_estride = (int64_t)H * F;
+  p.C = h; p.C2 = a; p.C3 = u; p.ldc = F;
+  p.N = F; p.K = H;
+  p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
+  const int bn = F % 128 == 0 ? 128 : 64;
+  const dim3 grid((unsigned)g.grid_m, (unsigned)(F / bn));
+  const bool save = a != nullptr;
+  return dtype == MOE_BF16 ? up_swiglu_t<bf16_t>(p, grid, bn, save, st)
+                           : up_swiglu_t<float>(p, grid, bn, save, st);
+}
+
+hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd, void* O, int H,
+                     int F, hipStream_t st) {
+  if (g.grid_m == 0) return hipSuccess;
+  Params p{};
+  p.A = h; p.lda = F;
+  p.B = Wd; p.ldb = H; p.b_estride = (int64_t)F * H;
+  p.C = O; p.ldc = H;
+  p.N = H; p.K = F;
+  p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
+  const int bn = pick_bn(H, true);
+  const dim3 grid((unsigned)g.grid_m, (unsigned)(H / bn));
+  return dtype == MOE_BF16 ? down_t<bf16_t>(p, grid, bn, st) : down_t<float>(p, grid, bn, st);
+}
+
+hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bias, float* logits,
+                       int64_t N, int H, int E, hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  Params p{};
+  p.A = X; p.lda = H;
+  p.B = Wr; p.ldb = E;
+  p.C = logits; p.ldc = E;
+  p.M = (int)N; p.N = E; p.K = H;
+  p.bias = bias;
+  const dim3 grid((unsigned)ceil_div(N, 128), (unsigned)ceil_div(E, 64));
+  return dtype == MOE_BF16
+             ? launch<bf16_t, Mode::Dense, 128, 64, false, true, false, false, Epi::BiasF32>(p, grid, st)
+             : launch<float, Mode::Dense, 128, 64, false, true, false, false, Epi::BiasF32>(p, grid, st);
+}
+
+}  // namespace moe

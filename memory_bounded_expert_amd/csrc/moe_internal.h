@@ -1,0 +1,139 @@
+// Internal interfaces of libmoebound: chunk geometry, workspace layout and
+// the kernel launchers.  Host code only; nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moebound.h"
+
+namespace moe {
+
+// Rows of one M-tile of the row-grouped GEMMs; the planner emits its tile
+// lists in this granularity.
+constexpr int kRowTile = 128;
+// Tokens per planner block: one wave, one 64-bit membership mask per expert.
+constexpr int kPlanBlock = 64;
+constexpr uint32_t kPlanMagic = 0x4d4f4542u;  // "MOEB"
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Chunk i of K over N tokens (strided membership: tokens i, i+K, ...).
+struct ChunkGeom {
+  int64_t n;          // tokens in the chunk, ceil((N - i) / K)
+  int64_t pair_base;  // k * (tokens in chunks 0..i-1)
+};
+inline ChunkGeom chunk_geom(int64_t N, int64_t K, int64_t k, int64_t i) {
+  const int64_t q = N / K, rem = N % K;
+  ChunkGeom g;
+  g.n = q + (i < rem ? 1 : 0);
+  g.pair_base = k * (i * q + (i < rem ? i : rem));
+  return g;
+}
+
+inline int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+// Upper bound on the row-grouped GEMM's M-tiles for a chunk of R pairs:
+// sum_e ceil(M_e / T) <= R / T + (number of non-empty experts).
+inline int64_t max_row_tiles(int64_t R, int E) {
+  return R / kRowTile + (R < E ? R : E);
+}
+
+// Byte offsets of the workspace regions (each 256-byte aligned).
+struct Layout {
+  size_t logits = 0;      // [N][E] f32, forward only, when the caller passes none
+  size_t rank = 0;        // [N*k] i32  rank of a pair inside its planner block
+  size_t blk = 0;         // [K][nblk][E] i32 block counts, then block bases
+  size_t offsets = 0;     // [K][E+1] i32
+  size_t tiles = 0;       // [K][max_tiles] int2 (expert, first row)
+  size_t tile_count = 0;  // [K] i32
+  size_t perm = 0;        // [N*k] i32
+  size_t pos = 0;         // [N*k] i32
+  size_t xp = 0;          // [k c_eff][H]  permuted inputs (dispatch buffer 1)
+  size_t o = 0;           // [k c_eff][H]  expert outputs / dY rows, then dXp (buffer 2)
+  size_t h = 0;           // [k c_eff][F]  h (forward); h, then g*h (backward)
+  size_t a = 0;           // [k c_eff][F]  backward: a, then da
+  size_t u = 0;           // [k c_eff][F]  backward: u, then du
+  size_t dh = 0;          // [k c_eff][F] f32 backward: dY W_down^T
+  size_t wrt = 0;         // [E][H] backward: W_r transposed
+  size_t dgates = 0;      // [N*k] f32 backward, when the caller passes none
+  size_t total = 0;
+  int64_t nblk = 0;
+  int64_t max_tiles = 0;
+};
+
+enum class Pass { Forward, Backward, Debug };
+Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_dgates);
+
+// ---- launchers (all asynchronous on `st`; return the first enqueue error)
+hipError_t launch_topk(const float* logits, int64_t N, int E, int k, int32_t* idx, float* gates,
+                       hipStream_t st);
+
+struct PlanBuffers {
+  int32_t* rank;
+  int32_t* blk;
+  int32_t* offsets;
+  int2* tiles;
+  int32_t* tile_count;
+  int32_t* perm;
+  int32_t* pos;
+  int64_t nblk;
+  int64_t max_tiles;
+};
+// Plans every chunk at once: counts, scans and scatters the whole batch's
+// routed pairs (O(N k) int32, nothing H-wide).  3 launches.
+hipError_t launch_plan(const int32_t* idx, int64_t N, int K, int k, int E, const PlanBuffers& b,
+                       hipStream_t st);
+
+// Data movement (dtype-dispatched: 0 f32, 1 bf16).
+hipError_t launch_gather(int dtype, const void* src, void* dst, const int32_t* perm_chunk, int64_t R,
+                         int k, int64_t N, int H, hipStream_t st);
+hipError_t launch_combine(int dtype, const void* O, const int32_t* pos, const float* gates, void* Y,
+                          int64_t N, int K, int i, int64_t n_i, int k, int H, hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_transpose(int dtype, const void* src, void* dst, int rows, int cols,
+                            hipStream_t st);
+hipError_t launch_swiglu_bwd(int dtype, const float* dh, void* a_da, void* u_du, void* h_hg,
+                             const int32_t* perm_chunk, const float* gates, float* dgates,
+                             int64_t R, int F, int64_t Nk, hipStream_t st);
+hipError_t launch_combine_bwd(int dtype, const void* dXp, const void* WrT, const int32_t* idx,
+                              const int32_t* pos, const float* gates, const float* dgates,
+                              void* dX, float* dlogits, int64_t N, int K, int i, int64_t n_i,
+                              int k, int E, int H, hipStream_t st);
+hipError_t launch_dwr(int dtype, const void* Xp, const int32_t* perm_chunk, const int32_t* offsets,
+                      const float* dlogits, float* dWr, int k, int E, int H, int64_t N,
+                      hipStream_t st);
+
+// GEMMs (see gemm.hip for the tile scheme).
+struct RowsGeom {
+  const int2* tiles;
+  const int32_t* tile_count;
+  const int32_t* offsets;
+  int64_t grid_m;  // upper bound on the chunk's M-tiles
+};
+// h = silu(Xp W_gate[e]) * (Xp W_up[e]) per expert segment; save_au also
+// stores a and u.
+hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const void* Wg,
+                          const void* Wu, void* h, void* a, void* u, int H, int F, hipStream_t st);
+// O = h W_down[e]
+hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd, void* O, int H,
+                     int F, hipStream_t st);
+// dh = dYp W_down[e]^T (fp32 out)
+hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd, float* dh, int H,
+                   int F, hipStream_t st);
+// dXp = da W_gate[e]^T + du W_up[e]^T
+hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du, const void* Wg,
+                   const void* Wu, void* dXp, int H, int F, hipStream_t st);
+// dW_gate[e] += Xp_e^T da_e, dW_up[e] += Xp_e^T du_e
+hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, const void* da,
+                         const void* du, float* dWg, float* dWu, int E, int H, int F,
+                         hipStream_t st);
+// dW_down[e] += hg_e^T dYp_e
+hipError_t gemm_wgrad_d(int dtype, const int32_t* offsets, const void* hg, const void* dYp,
+                        float* dWd, int E, int H, int F, hipStream_t st);
+// logits = X W_r (+ bias), fp32 out
+hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bias, float* logits,
+                       int64_t N, int H, int E, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,117 @@
+// Router top-k and gates: one wave64 per token.
+//
+// Each token selects its top-k experts ("Memory-Efficient Expert Routing for
+// Distributed MoE Training", section 2.1).  Slot s holds the s-th expert in
+// the order (logit descending, expert index ascending); IEEE comparison, so
+// -0.0 and +0.0 tie and the lower index wins.  The gates are the softmax of
+// the logits restricted to the selected experts, which equals the softmax over
+// all E experts restricted and renormalised ("896 routed experts, 16
+// activated": "Training Trillion-Parameter MoE ...", section 1, is the widest
+// shape served).
+#include "device_common.hpp"
+#include "moe_internal.h"
+
+#include <climits>
+
+namespace moe {
+namespace {
+
+struct Cand {
+  float v;
+  int i;  // INT_MAX: no candidate
+};
+
+// (v, i) beats (w, j) when v > w, or v and w do not compare greater either
+// way (equal, or +0/-0) and i < j.
+__device__ __forceinline__ bool beats(float v, int i, float w, int j) {
+  if (i == INT_MAX) return false;
+  if (j == INT_MAX) return true;
+  if (v > w) return true;
+  if (w > v) return false;
+  return i < j;
+}
+
+template <int VPL>
+__global__ __launch_bounds__(kThreads) void topk_gates_kernel(const float* __restrict__ logits,
+                                                              int64_t N, int E, int k,
+                                                              int32_t* __restrict__ idx,
+                                                              float* __restrict__ gates) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= N) return;  // whole wave leaves together
+  const float* row = logits + t * E;
+  float v[VPL];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = 0.f;
+    if (e < E) {
+      v[j] = row[e];
+      avail |= 1u << j;
+    }
+  }
+  float my_v = 0.f;
+  int my_i = 0;
+  for (int s = 0; s < k; ++s) {
+    float bv = 0.f;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      // j ascending visits this lane's experts in ascending order, so a
+      // strict comparison keeps the lower index on ties
+      if ((avail >> j) & 1u) {
+        if (bi == INT_MAX || v[j] > bv) {
+          bv = v[j];
+          bi = lane + 64 * j;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (beats(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == (bi & 63)) avail &= ~(1u << (bi >> 6));
+    if (lane == s) {
+      my_v = bv;
+      my_i = bi;
+    }
+  }
+  const float top = __shfl(my_v, 0, 64);
+  float ex = lane < k ? expf(my_v - top) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if (lane < k) {
+    idx[t * k + lane] = my_i;
+    gates[t * k + lane] = ex / sum;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float* logits, int64_t N, int E, int k, int32_t* idx, float* gates,
+                       hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  const int per_block = kThreads / 64;
+  const dim3 grid((unsigned)((N + per_block - 1) / per_block));
+  const int vpl = (E + 63) / 64;
+  if (vpl <= 1)
+    topk_gates_kernel<1><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates);
+  else if (vpl <= 2)
+    topk_gates_kernel<2><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates);
+  else if (vpl <= 4)
+    topk_gates_kernel<4><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates);
+  else if (vpl <= 8)
+    topk_gates_kernel<8><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates);
+  else
+    topk_gates_kernel<16><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates);
+  return hipGetLastError();
+}
+
+}  // namespace moe

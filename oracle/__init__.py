@@ -20,6 +20,9 @@ from .moe_oracle import (  # noqa: F401
     moe_forward,
     forward_tokens,
     moe_backward,
+    expert_grads,
+    router_grads,
+    backward_tokens,
     logit_error_bound,
     dispatch_bound_bytes,
 )

@@ -246,19 +246,49 @@ def forward_tokens(x_rows, idx_rows, gate_rows, experts: Callable[[int], Tuple])
     return out
 
 
-def moe_backward(X, Wr, Wg, Wu, Wd, dY, idx, gates):
-    """Gradients of L = <Y, dY> with the selection held constant.
-
-    With a = x W_g, u = x W_u, h = silu(a) u, o = h W_d and y = sum_s g_s o_s:
-      dL/dg_s    = <dY_t, o_s>
-      dh         = g_s dY_t W_d^T
+def expert_grads(x, dy, g, wg, wu, wd):
+    """Gradients carried by the rows routed to one expert (rows of x, their
+    upstream rows dy and gates g), with L = <Y, dY>:
+      o = (silu(a) * u) W_d,  a = x W_g,  u = x W_u
+      dL/dg      = <dy, o>
+      dh         = g dy W_d^T
       da         = dh * u * sigma(a) (1 + a (1 - sigma(a))),   du = dh * silu(a)
-      dW_d[e]   += h^T (g dY),  dW_g[e] += x^T da,  dW_u[e] += x^T du
-      dx_t      += da W_g^T + du W_u^T
-    and for the gates g_j = exp(l_j) / sum_{S_t} exp(l) (the full softmax's
+      dW_d      += h^T (g dy),  dW_g += x^T da,  dW_u += x^T du
+      dx        += da W_g^T + du W_u^T
+    Returns (dx_rows, dWg, dWu, dWd, dgate_rows)."""
+    x = np.asarray(x, f64)
+    dy = np.asarray(dy, f64)
+    g = np.asarray(g, f64)[:, None]
+    wg, wu, wd = (np.asarray(w, f64) for w in (wg, wu, wd))
+    a = x @ wg
+    u = x @ wu
+    sa = sigmoid(a)
+    h = a * sa * u
+    o = h @ wd
+    dgate = np.sum(dy * o, axis=1)
+    dh = g * (dy @ wd.T)
+    dWd = h.T @ (g * dy)
+    da = dh * u * sa * (1.0 + a * (1.0 - sa))
+    du = dh * a * sa
+    return da @ wg.T + du @ wu.T, x.T @ da, x.T @ du, dWd, dgate
+
+
+def router_grads(gates, dgates, idx, E: int) -> np.ndarray:
+    """dlogits for gates g_j = exp(l_j) / sum_{S_t} exp(l) (the full softmax's
     normaliser cancels in the renormalisation):
-      dl_j = g_j (dg_j - sum_j' g_j' dg_j') on the selected experts, 0 elsewhere,
-      dx_t += dl_t W_r^T,  dW_r = X^T dl.
+      dl_j = g_j (dg_j - sum_j' g_j' dg_j') on the selected experts, 0 elsewhere."""
+    gates = np.asarray(gates, f64)
+    dgates = np.asarray(dgates, f64)
+    dsel = gates * (dgates - np.sum(gates * dgates, axis=1, keepdims=True))
+    dl = np.zeros((gates.shape[0], E), f64)
+    np.put_along_axis(dl, np.asarray(idx, np.int64), dsel, axis=1)
+    return dl
+
+
+def moe_backward(X, Wr, Wg, Wu, Wd, dY, idx, gates):
+    """Gradients of L = <Y, dY> with the selection held constant: the expert
+    part of every routed pair (expert_grads), then the router part
+    (router_grads), dx_t += dl_t W_r^T and dW_r = X^T dl.
     Returns dict with dX, dWg, dWu, dWd, dlogits, dgates, dWr."""
     X = np.asarray(X, f64)
     dY = np.asarray(dY, f64)
@@ -279,29 +309,35 @@ def moe_backward(X, Wr, Wg, Wu, Wd, dY, idx, gates):
         rows_t, rows_s = np.nonzero(idx == e)
         if len(rows_t) == 0:
             continue
-        wg, wu, wd = experts(e)
-        x = X[rows_t]
-        a = x @ wg
-        u = x @ wu
-        sa = sigmoid(a)
-        h = a * sa * u
-        o = h @ wd
-        dy = dY[rows_t]
-        g = gates[rows_t, rows_s][:, None]
-        dgates[rows_t, rows_s] = np.sum(dy * o, axis=1)
-        dh = g * (dy @ wd.T)
-        dWd[e] = h.T @ (g * dy)
-        da = dh * u * sa * (1.0 + a * (1.0 - sa))
-        du = dh * a * sa
-        dWg[e] = x.T @ da
-        dWu[e] = x.T @ du
-        dX[rows_t] += da @ wg.T + du @ wu.T
-    dsel = gates * (dgates - np.sum(gates * dgates, axis=1, keepdims=True))
-    dlogits = np.zeros((N, E), f64)
-    np.put_along_axis(dlogits, idx, dsel, axis=1)
+        dx, dWg[e], dWu[e], dWd[e], dg = expert_grads(
+            X[rows_t], dY[rows_t], gates[rows_t, rows_s], *experts(e))
+        dgates[rows_t, rows_s] = dg
+        dX[rows_t] += dx
+    dlogits = router_grads(gates, dgates, idx, E)
     dX += dlogits @ Wr.T
     dWr = X.T @ dlogits
     return dict(dX=dX, dWg=dWg, dWu=dWu, dWd=dWd, dlogits=dlogits, dgates=dgates, dWr=dWr)
+
+
+def backward_tokens(x_rows, dy_rows, idx_rows, gate_rows, experts: Callable[[int], Tuple], Wr):
+    """dX, dgates and dlogits of a few tokens, one at a time (sampled checks
+    at sizes where the full oracle is too slow).  Returns (dX, dgates, dlogits)."""
+    x_rows = np.asarray(x_rows, f64)
+    dy_rows = np.asarray(dy_rows, f64)
+    Wr = np.asarray(Wr, f64)
+    n, k = idx_rows.shape
+    E = Wr.shape[1]
+    dX = np.zeros_like(x_rows)
+    dg = np.zeros((n, k), f64)
+    for r in range(n):
+        for s in range(k):
+            dx, _, _, _, d = expert_grads(x_rows[r:r + 1], dy_rows[r:r + 1],
+                                          np.asarray(gate_rows[r:r + 1, s]), *experts(int(idx_rows[r, s])))
+            dX[r] += dx[0]
+            dg[r, s] = d[0]
+    dl = router_grads(gate_rows, dg, idx_rows, E)
+    dX += dl @ Wr.T
+    return dX, dg, dl
 
 
 # ----------------------------------------------------------------------------

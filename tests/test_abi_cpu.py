@@ -1,0 +1,161 @@
+"""The C ABI on the host, without a GPU: the library loads and exports every
+function the header declares, the structs match the C layout, the chunk plan
+matches the oracle's eq. (1), and argument errors come back before anything
+is enqueued."""
+
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from memory_bounded_expert_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libmoebound.so not built (run __graft_entry__.build())")
+
+
+def test_exports_every_declared_function():
+    names = B.declared_functions()
+    assert set(names) == {"moe_plan_chunks", "moe_bounded_forward", "moe_bounded_backward",
+                          "moe_status_string", "moe_debug_topk", "moe_debug_plan",
+                          "moe_debug_stage"}
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_c():
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "moebound.h"
+#define O(s, f) printf("%s.%s %zu\n", #s, #f, offsetof(s, f));
+int main(void) {
+  printf("plan %zu\nstats %zu\n", sizeof(moe_plan_t), sizeof(moe_stats_t));
+  O(moe_plan_t, N) O(moe_plan_t, K) O(moe_plan_t, c_eff) O(moe_plan_t, debug_workspace_bytes)
+  O(moe_stats_t, c_eff) O(moe_stats_t, workspace_bytes)
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "t")
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        c, "-o", exe], check=True)
+        lines = dict(l.rsplit(" ", 1) for l in subprocess.run([exe], capture_output=True,
+                                                              text=True).stdout.splitlines())
+    assert int(lines["plan"]) == ctypes.sizeof(B.MoePlan)
+    assert int(lines["stats"]) == ctypes.sizeof(B.MoeStats)
+    for f in ("N", "K", "c_eff", "debug_workspace_bytes"):
+        assert int(lines[f"moe_plan_t.{f}"]) == getattr(B.MoePlan, f).offset
+    for f in ("c_eff", "workspace_bytes"):
+        assert int(lines[f"moe_stats_t.{f}"]) == getattr(B.MoeStats, f).offset
+
+
+def test_plan_matches_oracle_exhaustively():
+    for N in range(0, 200):
+        for c in range(1, N + 3, max(1, N // 15)):
+            for K_max in (1, 2, 3, 5, 8, 13, 20):
+                p = B.moe_plan_chunks(N, 64, 64, 8, 2, c, K_max, B.MOE_F32)
+                K, ce = oracle.plan_chunks(N, c, K_max)
+                assert (p.K, p.c_eff) == (K, ce), (N, c, K_max)
+                assert p.max_pairs_per_chunk == 2 * ce
+                assert p.dispatch_bound_bytes == oracle.dispatch_bound_bytes(2, ce, 64, 4)
+
+
+def test_plan_page_instance_and_workloads():
+    p = B.moe_plan_chunks(65536, 7168, 2048, 64, 8, 6554, 10, B.MOE_BF16)
+    assert (p.K, p.c_eff) == (10, 6554)
+    expect = {  # (N, c, K_max) -> (K, c_eff)
+        (256, 64, 8): (4, 64), (4096, 1024, 8): (4, 1024), (16384, 2048, 16): (8, 2048),
+        (8192, 1024, 8): (8, 1024), (65536, 4096, 16): (16, 4096),
+    }
+    for (N, c, K_max), kc in expect.items():
+        assert oracle.plan_chunks(N, c, K_max) == kc
+        q = B.moe_plan_chunks(N, 2048, 1024, 64, 8, c, K_max, B.MOE_BF16)
+        assert (q.K, q.c_eff) == kc
+
+
+def test_workspace_bounded_by_chunk_not_batch():
+    # the H-wide per-chunk buffers scale with c_eff, not N
+    a = B.moe_plan_chunks(65536, 2048, 1024, 64, 8, 4096, 16, B.MOE_BF16)
+    b = B.moe_plan_chunks(65536, 2048, 1024, 64, 8, 4096, 1, B.MOE_BF16)
+    assert a.dispatch_bound_bytes * 16 == b.dispatch_bound_bytes
+    assert a.fwd_workspace_bytes < b.fwd_workspace_bytes / 6
+    assert a.bwd_workspace_bytes < b.bwd_workspace_bytes / 6
+    assert a.dispatch_bound_bytes == 2 * 8 * 4096 * 2048 * 2
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 64, 64, 8, 2, 4, 4, 0), B.MOE_EINVAL),     # N < 0
+    ((10, 64, 64, 8, 2, 0, 4, 0), B.MOE_EINVAL),     # c = 0
+    ((10, 64, 64, 8, 2, 4, 0, 0), B.MOE_EINVAL),     # K_max = 0
+    ((10, 64, 64, 8, 0, 4, 4, 0), B.MOE_EINVAL),     # k = 0
+    ((10, 64, 64, 8, 9, 4, 4, 0), B.MOE_EINVAL),     # k > E
+    ((10, 64, 64, 8, 2, 4, 4, 7), B.MOE_EINVAL),     # dtype
+    ((10, 0, 64, 8, 2, 4, 4, 0), B.MOE_EINVAL),      # H = 0
+    ((10, 96, 64, 8, 2, 4, 4, 0), B.MOE_EUNSUPPORTED),   # H % 64
+    ((10, 64, 96, 8, 2, 4, 4, 0), B.MOE_EUNSUPPORTED),   # F % 64
+    ((10, 64, 64, 12, 2, 4, 4, 1), B.MOE_EUNSUPPORTED),  # E % 8 for bf16
+    ((10, 64, 64, 2048, 2, 4, 4, 0), B.MOE_EUNSUPPORTED),  # E > 1024
+    ((10, 64, 64, 128, 65, 4, 4, 0), B.MOE_EUNSUPPORTED),  # k > 64
+    ((2**28, 64, 64, 16, 8, 4, 4, 0), B.MOE_EUNSUPPORTED),  # N k >= 2^31
+])
+def test_plan_errors(args, status):
+    plan = B.MoePlan()
+    assert B.lib().moe_plan_chunks(*args, ctypes.byref(plan)) == status
+
+
+def test_empty_batch_is_noop():
+    p = B.moe_plan_chunks(0, 64, 64, 8, 2, 4, 4, B.MOE_F32)
+    assert (p.K, p.c_eff, p.fwd_workspace_bytes, p.dispatch_bound_bytes) == (0, 0, 0, 0)
+    st = B.MoeStats()
+    assert B.lib().moe_bounded_forward(ctypes.byref(p), *([None] * 10), None, 0, None,
+                                       ctypes.byref(st)) == B.MOE_OK
+    assert st.K == 0 and st.launches == 0
+
+
+def test_forward_argument_errors_before_any_launch():
+    L = B.lib()
+    p = B.moe_plan_chunks(256, 64, 128, 8, 2, 64, 8, B.MOE_F32)
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: every check below fails first
+    ptrs = [fake] * 10
+    # a plan that did not come from moe_plan_chunks
+    bad = B.MoePlan()
+    assert L.moe_bounded_forward(ctypes.byref(bad), *ptrs, fake, 1 << 30, None, None) == B.MOE_EINVAL
+    # a required pointer missing
+    miss = list(ptrs)
+    miss[0] = None
+    assert L.moe_bounded_forward(ctypes.byref(p), *miss, fake, 1 << 30, None, None) == B.MOE_EINVAL
+    # misaligned workspace
+    assert L.moe_bounded_forward(ctypes.byref(p), *ptrs, ctypes.c_void_p(0x100010), 1 << 30, None,
+                                 None) == B.MOE_EINVAL
+    # workspace one byte short
+    assert L.moe_bounded_forward(ctypes.byref(p), *ptrs, fake, p.fwd_workspace_bytes - 1, None,
+                                 None) == B.MOE_EWORKSPACE
+    bptrs = [fake] * 15
+    assert L.moe_bounded_backward(ctypes.byref(p), *bptrs, fake, p.bwd_workspace_bytes - 1, None,
+                                  None) == B.MOE_EWORKSPACE
+    assert L.moe_debug_plan(ctypes.byref(p), fake, fake, fake, fake, fake,
+                            p.debug_workspace_bytes - 1, None) == B.MOE_EWORKSPACE
+    assert L.moe_debug_stage(ctypes.byref(p), 4, 0, *ptrs[:9], fake, p.fwd_workspace_bytes - 1,
+                             None) == B.MOE_EWORKSPACE
+    assert L.moe_debug_stage(ctypes.byref(p), 9, 0, *ptrs[:9], fake, 1 << 30, None) == B.MOE_EINVAL
+    assert L.moe_debug_stage(ctypes.byref(p), 4, p.K, *ptrs[:9], fake, 1 << 30, None) == B.MOE_EINVAL
+    assert L.moe_debug_topk(fake, 4, 8, 9, fake, fake, None) == B.MOE_EINVAL
+    assert L.moe_debug_topk(fake, 4, 2048, 9, fake, fake, None) == B.MOE_EUNSUPPORTED
+
+
+def test_status_strings():
+    for s in range(0, 6):
+        assert isinstance(B.status_string(s), str) and B.status_string(s)

@@ -1,0 +1,193 @@
+"""End-to-end parity of the HIP layer against the fp64 oracle, through the C ABI.
+
+For each workload:
+  * a reduced batch (ragged strided chunks, several GEMM tiles) against the
+    full unchunked oracle: routing bit-exact on the GPU's logits, outputs to
+    max|gpu - oracle| / max|oracle| <= 1e-2 (bf16) or 1e-5 (fp32);
+  * the full batch in the launch configuration the benchmark times: routing
+    for every token, outputs on sampled tokens (and, for backward, the weight
+    gradients of sampled experts) evaluated one by one by the oracle;
+  * chunked == unchunked: the same call with K_max = 1 gives bitwise equal
+    per-token outputs; two runs give bitwise equal results;
+  * the dispatch buffers stay within 2 k c_eff H b.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from gpu_common import (BF16_TOL, DEV, F32_TOL, DevInputs, backward, check_routing, dev_to_f64,
+                        forward, needs_gpu, plan_for, rel_err, require_lib, say)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+# reduced batch: (N, c) keeping the workload's K and a ragged last chunk
+REDUCED = {
+    "tiny_f32": (256, 64),
+    "balanced_bf16": (1003, 251),
+    "zipf_bf16": (301, 38),
+    "many_experts_bf16": (515, 65),
+    "train_bf16": (777, 49),
+}
+
+
+def _oracle_fwd(inp, X64, idx):
+    Y, _, g, _ = oracle.moe_forward(X64, inp.f64("Wr"), inp.bias, inp.expert_f64, None, None,
+                                    inp.wl.k, idx=idx)
+    return Y, g
+
+
+def _sub(d, n):
+    sub = DevInputs.__new__(DevInputs)
+    sub.__dict__.update(d.__dict__)
+    sub.X = d.X[:n].contiguous()
+    sub.dY = None if d.dY is None else d.dY[:n].contiguous()
+    return sub
+
+
+def _sample_tokens(N, n=40, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, N - 1], rng.choice(N, n, replace=False)]))
+
+
+def run_workload(name, full=True):
+    require_lib()
+    wl = datagen.WORKLOADS[name]
+    tol = F32_TOL if wl.dtype == "f32" else BF16_TOL
+    b = 4 if wl.dtype == "f32" else 2
+    say(f"[{name}] generating inputs")
+    inp = datagen.Inputs(wl, progress=say)
+    d = DevInputs(inp)
+
+    # ---- reduced batch against the full oracle
+    n, c = REDUCED[name]
+    ds = _sub(d, n)
+    plan = plan_for(wl, N=n, c=c)
+    say(f"[{name}] reduced forward N={n} K={plan.K} c_eff={plan.c_eff}")
+    Y, idx, g, lg, st = forward(ds, plan)
+    idx_np = idx.cpu().numpy()
+    rows = np.arange(n)
+    check_routing(inp, lg.cpu().numpy(), idx_np, g.cpu().numpy(), rows=rows)
+    X64 = inp.to_f64(inp.X[:n])
+    Yref, gref = _oracle_fwd(inp, X64, idx_np)
+    err = rel_err(dev_to_f64(Y), Yref)
+    say(f"[{name}] reduced Y rel err {err:.3e}")
+    assert err <= tol
+    assert st["dispatch_bytes"] <= oracle.dispatch_bound_bytes(wl.k, plan.c_eff, wl.H, b)
+    # chunked == unchunked, bitwise
+    p1 = plan_for(wl, N=n, c=c, K_max=1)
+    Y1, idx1, g1, lg1, _ = forward(ds, p1)
+    assert torch.equal(lg, lg1) and torch.equal(idx, idx1) and torch.equal(g, g1)
+    assert torch.equal(Y.view(torch.int16) if Y.dtype == torch.bfloat16 else Y,
+                       Y1.view(torch.int16) if Y1.dtype == torch.bfloat16 else Y1)
+
+    if wl.backward:
+        say(f"[{name}] reduced backward")
+        out = backward(ds, plan, idx, g)
+        ref = oracle.moe_backward(X64, inp.f64("Wr"), inp.expert_f64, None, None,
+                                  inp.to_f64(inp.dY[:n]), idx_np, g.cpu().numpy().astype(np.float64))
+        for key, rk in (("dX", "dX"), ("dW_gate", "dWg"), ("dW_up", "dWu"), ("dW_down", "dWd"),
+                        ("dlogits", "dlogits"), ("dgates", "dgates"), ("dW_r", "dWr")):
+            e_ = rel_err(dev_to_f64(out[key]), ref[rk])
+            say(f"[{name}]   {key} rel err {e_:.3e}")
+            assert e_ <= tol, key
+        out1 = backward(ds, p1, idx, g)
+        for key in ("dX", "dlogits", "dgates"):
+            assert torch.equal(out[key].view(torch.int16) if out[key].dtype == torch.bfloat16
+                               else out[key],
+                               out1[key].view(torch.int16) if out1[key].dtype == torch.bfloat16
+                               else out1[key]), key
+        for key in ("dW_gate", "dW_up", "dW_down"):
+            dk = rel_err(dev_to_f64(out[key]), dev_to_f64(out1[key]))
+            say(f"[{name}]   {key} chunked vs unchunked {dk:.2e}")
+            assert dk <= 1e-5
+        again = backward(ds, plan, idx, g)
+        for key in ("dX", "dW_gate", "dW_up", "dW_down", "dlogits", "dgates", "dW_r"):
+            assert torch.equal(again[key], out[key]), key
+        del out, out1, again
+
+    if not full or n == wl.N:
+        return
+    # ---- full batch, sampled tokens
+    plan = plan_for(wl)
+    say(f"[{name}] full forward N={wl.N} K={plan.K} c_eff={plan.c_eff}")
+    Y, idx, g, lg, st = forward(d, plan)
+    idx_np = idx.cpu().numpy()
+    flips = check_routing(inp, lg.cpu().numpy(), idx_np, g.cpu().numpy())
+    say(f"[{name}] routing ok, {flips} tokens flipped within the fp32 bound")
+    toks = _sample_tokens(wl.N)
+    X64 = inp.to_f64(inp.X[toks])
+    l64 = oracle.router_logits(X64, inp.f64("Wr"), inp.bias)
+    gt = oracle.gates_from_logits(l64, idx_np[toks])
+    Yt = oracle.forward_tokens(X64, idx_np[toks], gt, inp.expert_f64)
+    err = rel_err(dev_to_f64(Y[torch.from_numpy(toks).to(DEV)]), Yt)
+    say(f"[{name}] full Y rel err on {len(toks)} sampled tokens {err:.3e}")
+    assert err <= tol
+    assert st["dispatch_bytes"] == oracle.dispatch_bound_bytes(wl.k, plan.c_eff, wl.H, b)
+    Y2, idx2, g2, lg2, _ = forward(d, plan)
+    assert torch.equal(Y, Y2) and torch.equal(idx, idx2) and torch.equal(lg, lg2)
+    del Y2, idx2, g2, lg2
+    p1 = plan_for(wl, K_max=1)
+    say(f"[{name}] full forward unchunked")
+    Y1, idx1, g1, lg1, st1 = forward(d, p1)
+    assert torch.equal(idx, idx1) and torch.equal(g, g1)
+    assert torch.equal(Y.view(torch.int16), Y1.view(torch.int16))
+    say(f"[{name}] dispatch bytes {st['dispatch_bytes']} (unchunked {st1['dispatch_bytes']})")
+    del Y1, idx1, g1, lg1
+    torch.cuda.empty_cache()
+
+    if wl.backward:
+        say(f"[{name}] full backward")
+        out = backward(d, plan, idx, g)
+        dYt = inp.to_f64(inp.dY[toks])
+        dXt, dgt, dlt = oracle.backward_tokens(X64, dYt, idx_np[toks],
+                                               g.cpu().numpy()[toks].astype(np.float64),
+                                               inp.expert_f64, inp.f64("Wr"))
+        tsel = torch.from_numpy(toks).to(DEV)
+        for key, ref in (("dX", dXt), ("dgates", dgt), ("dlogits", dlt)):
+            e_ = rel_err(dev_to_f64(out[key][tsel]), ref)
+            say(f"[{name}]   sampled {key} rel err {e_:.3e}")
+            assert e_ <= tol, key
+        gnp = g.cpu().numpy().astype(np.float64)
+        counts = np.bincount(idx_np.reshape(-1), minlength=wl.E)
+        for e in sorted({int(np.argmax(counts)), int(np.argmin(counts)), 7 % wl.E}):
+            rt, rs = np.nonzero(idx_np == e)
+            _, dWg, dWu, dWd, _ = oracle.expert_grads(inp.to_f64(inp.X[rt]), inp.to_f64(inp.dY[rt]),
+                                                      gnp[rt, rs], *inp.expert_f64(e))
+            for key, ref in (("dW_gate", dWg), ("dW_up", dWu), ("dW_down", dWd)):
+                e_ = rel_err(dev_to_f64(out[key][e]), ref)
+                say(f"[{name}]   expert {e} ({counts[e]} rows) {key} rel err {e_:.3e}")
+                assert e_ <= tol, (key, e)
+        p1 = plan_for(wl, K_max=1)
+        say(f"[{name}] full backward unchunked")
+        out1 = backward(d, p1, idx, g)
+        for key in ("dX", "dlogits", "dgates"):
+            a, b_ = out[key], out1[key]
+            if a.dtype == torch.bfloat16:
+                a, b_ = a.view(torch.int16), b_.view(torch.int16)
+            assert torch.equal(a, b_), key
+        for key in ("dW_gate", "dW_up", "dW_down", "dW_r"):
+            say(f"[{name}]   {key} chunked vs unchunked "
+                f"{rel_err(dev_to_f64(out[key]), dev_to_f64(out1[key])):.2e}")
+
+
+def test_tiny_f32():
+    run_workload("tiny_f32")
+
+
+def test_balanced_bf16():
+    run_workload("balanced_bf16")
+
+
+def test_many_experts_bf16():
+    run_workload("many_experts_bf16")
+
+
+def test_zipf_bf16():
+    run_workload("zipf_bf16")
+
+
+def test_train_bf16():
+    run_workload("train_bf16")

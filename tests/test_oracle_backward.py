@@ -99,3 +99,20 @@ def test_router_gradient_invariants():
     _, idx1, g1, _ = oracle.moe_forward(X, Wr, None, Wg, Wu, Wd, 1)
     d1 = oracle.moe_backward(X, Wr, Wg, Wu, Wd, dY, idx1, g1)
     assert np.all(d1["dlogits"] == 0.0) and np.all(d1["dWr"] == 0.0)
+
+
+def test_backward_tokens_and_expert_grads_match_layer():
+    X, Wr, Wg, Wu, Wd, dY, k = problem(14, N=20, E=6, k=3)
+    _, idx, g, _ = oracle.moe_forward(X, Wr, None, Wg, Wu, Wd, k)
+    d = oracle.moe_backward(X, Wr, Wg, Wu, Wd, dY, idx, g)
+    rows = [0, 7, 19]
+    experts = lambda e: (Wg[e], Wu[e], Wd[e])
+    dx, dg, dl = oracle.backward_tokens(X[rows], dY[rows], idx[rows], g[rows], experts, Wr)
+    np.testing.assert_allclose(dx, d["dX"][rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dg, d["dgates"][rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dl, d["dlogits"][rows], rtol=1e-12, atol=1e-13)
+    e = int(idx[7, 1])
+    rt, rs = np.nonzero(idx == e)
+    _, dWg, dWu, dWd, _ = oracle.expert_grads(X[rt], dY[rt], g[rt, rs], *experts(e))
+    np.testing.assert_allclose(dWg, d["dWg"][e], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dWd, d["dWd"][e], rtol=1e-12, atol=1e-13)
