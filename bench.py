@@ -138,37 +138,51 @@ def main():
     for i in range(K):
         toks = np.arange(i, N, K)
         chunks.append((len(toks), len(toks) * k, len(np.unique(idx_np[toks]))))
+    # whole-batch stages: events around repeated launches
     stages = {}
-    for stage in ("router", "topk", "plan", "gather", "gemm_up", "gemm_down", "combine"):
-        per_chunk = stage in ("gather", "gemm_up", "gemm_down", "combine")
-        targets = list(range(K)) if per_chunk else [0]
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for stage in ("router", "topk", "plan"):
+        e0, e1 = ev(), ev()
         e0.record(stream)
         for _ in range(args.stage_reps):
-            for i in targets:
-                B.moe_debug_stage(plan, stage, i, X, Wr, bias, Wg, Wu, Wd, Y, idx, gates, ws,
-                                  stream=stream)
+            B.moe_debug_stage(plan, stage, 0, X, Wr, bias, Wg, Wu, Wd, Y, idx, gates, ws,
+                              stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
-        launches = args.stage_reps * len(targets)
-        us = e0.elapsed_time(e1) * 1e3 / launches
-        rec = {"us_per_launch": round(us, 2), "launches_per_step": len(targets)}
-        if per_chunk:
-            byts = np.mean([stage_work(stage, wl, b, *c)[0] for c in chunks])
-            flops = np.mean([stage_work(stage, wl, b, *c)[1] for c in chunks])
-            rec["GB_per_s"] = round(byts / us / 1e3, 1)
-            rec["hbm_frac"] = round(byts / us / 1e3 / HBM_PEAK_GBS, 4)
-            rec["alg_bytes_per_launch"] = int(byts)
-            if stage.startswith("gemm"):
-                tf = flops / us / 1e6
-                peak = BF16_PEAK_TFLOPS if bf else FP32_PEAK_TFLOPS
-                rec["TFLOP_per_s"] = round(tf, 1)
-                rec["mfma_frac"] = round(tf / peak, 4)
-                rec["alg_flops_per_launch"] = int(flops)
-                rec["intensity_flop_per_B"] = round(flops / byts, 1)
+        stages[stage] = {"us_per_launch": round(e0.elapsed_time(e1) * 1e3 / args.stage_reps, 2),
+                         "launches_per_step": 1}
+    # per-chunk stages: replay the chunk loop in order (so every launch sees
+    # the same buffers as in the forward call), one event pair per launch
+    per_chunk = ("gather", "gemm_up", "gemm_down", "combine")
+    marks = {s_: [] for s_ in per_chunk}
+    for _ in range(args.stage_reps):
+        for i in range(K):
+            for stage in per_chunk:
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                B.moe_debug_stage(plan, stage, i, X, Wr, bias, Wg, Wu, Wd, Y, idx, gates, ws,
+                                  stream=stream)
+                e1.record(stream)
+                marks[stage].append((e0, e1))
+    torch.cuda.synchronize()
+    for stage in per_chunk:
+        us = float(np.mean([a.elapsed_time(b_) for a, b_ in marks[stage]])) * 1e3
+        rec = {"us_per_launch": round(us, 2), "launches_per_step": K}
+        byts = float(np.mean([stage_work(stage, wl, b, *c)[0] for c in chunks]))
+        flops = float(np.mean([stage_work(stage, wl, b, *c)[1] for c in chunks]))
+        rec["GB_per_s"] = round(byts / us / 1e3, 1)
+        rec["hbm_frac"] = round(byts / us / 1e3 / HBM_PEAK_GBS, 4)
+        rec["alg_bytes_per_launch"] = int(byts)
+        if stage.startswith("gemm"):
+            tf = flops / us / 1e6
+            peak = BF16_PEAK_TFLOPS if bf else FP32_PEAK_TFLOPS
+            rec["TFLOP_per_s"] = round(tf, 1)
+            rec["mfma_frac"] = round(tf / peak, 4)
+            rec["alg_flops_per_launch"] = int(flops)
+            rec["intensity_flop_per_B"] = round(flops / byts, 1)
         stages[stage] = rec
-        log(f"  {stage:10s} {us:9.2f} us/launch x {len(targets)}  {rec}")
+    for stage, rec in stages.items():
+        log(f"  {stage:10s} {rec}")
     # the forward call's outputs are unchanged by the re-launches
     Yc = Y.clone()
     step()

@@ -212,8 +212,10 @@ int moe_debug_plan(const moe_plan_t* plan, const int32_t* topk_idx,
  * with the same plan, inputs and outputs and logits == NULL; the workspace
  * still holds that call's routing plan.  The stage runs exactly the kernel
  * and launch configuration the forward call uses for chunk `chunk`
- * (0 <= chunk < plan->K), reading and writing the same buffers, so the
- * forward call's outputs are reproduced unchanged.
+ * (0 <= chunk < plan->K), reading and writing the same buffers.  Running
+ * GATHER, GEMM_UP, GEMM_DOWN and COMBINE for chunks 0..K-1 in that order
+ * reproduces the forward call's outputs bitwise; a stage run out of that
+ * order computes on whatever the per-chunk buffers hold.
  * stage: MOE_STAGE_ROUTER (router logits, whole batch), MOE_STAGE_TOPK (top-k
  *   and gates, whole batch), MOE_STAGE_PLAN (planner, whole batch),
  *   MOE_STAGE_GATHER, MOE_STAGE_GEMM_UP (gate/up GEMM + SwiGLU),

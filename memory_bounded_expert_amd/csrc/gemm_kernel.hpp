@@ -22,8 +22,10 @@
 // bank conflicts.  Operands stored K-contiguous in memory are copied 16 bytes
 // at a time; operands stored M/N-contiguous are loaded as 8 x 8 (bf16) or
 // 4 x 4 (fp32) blocks and transposed in registers on the way into LDS.
-// Two LDS stages: the global loads of K-tile t+1 are in flight while the
-// MFMAs consume tile t; one barrier per K-tile.
+// Two LDS stages fed from one (STAGES = 1) or two register stages: the
+// global loads of the next K-tile(s) are in flight while the MFMAs consume
+// the current one; one barrier per K-tile.  Operand loads are buffer loads
+// from per-tile resources, so ragged edges read zeros without branches.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16 for bf16 (fp32 accumulation), and for fp32
 // four v_mfma_f32_16x16x4_f32 per 16-byte chunk.  Every output element is
@@ -62,6 +64,28 @@ struct Params {
 };
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
+
+// Buffer resource over [base, base + bytes): a load whose offset lies past
+// `bytes` returns zeros, so ragged tiles need no branches.  Word 3 is the
+// gfx9 raw-buffer format (32-bit data, no swizzle).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = (int)(bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+constexpr uint32_t kOob = 0x7FFFFFF0u;  // an offset no resource covers
+// A pointer that is the same in every lane of the wave, moved to scalar
+// registers (the compiler cannot always prove the uniformity itself).
+template <typename P>
+__device__ __forceinline__ P* wave_uniform(P* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ u32x4_t bload(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
 
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
@@ -104,7 +128,8 @@ __device__ __forceinline__ void transpose_block(const u32x4_t* in, u32x4_t* out,
     out[c] = u32x4_t{word(in[0], c), word(in[1], c), word(in[2], c), word(in[3], c)};
 }
 
-template <typename T, Mode MODE, int BM, int BN, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
+template <typename T, Mode MODE, int BM, int BN, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI,
+          int STAGES = 1>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
   constexpr int EPC = Elem<T>::kPer16B;
   constexpr int BK = 8 * EPC;
@@ -122,6 +147,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
   static_assert(!A_K || (BM * 8) % kThreads == 0, "A tile / threads");
   static_assert(!B_K || (NCOL * 8) % kThreads == 0, "B tile / threads");
   static_assert(!(DUAL && KCAT), "DUAL and KCAT are exclusive");
+  // a B operand group must cover whole waves of loading threads
+  static_assert(!DUAL || (B_K ? (BN * 8) % 64 == 0 : (BN * 8 / EPC) % 64 == 0),
+                "operand group not wave-aligned");
 
   __shared__ u32x4_t As[2][BM * 8];
   __shared__ u32x4_t Bs[2][NCOL * 8];
@@ -148,16 +176,49 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
     m0 = blockIdx.x * BM;
     row_end = p.M;
   }
+  // The tile descriptor is the same for the whole work-group; make that
+  // visible so addresses and buffer resources stay in scalar registers.
+  e = __builtin_amdgcn_readfirstlane(e);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  row_end = __builtin_amdgcn_readfirstlane(row_end);
+  k_len = __builtin_amdgcn_readfirstlane(k_len);
+  k_begin = (int64_t)__builtin_amdgcn_readfirstlane((int)k_begin);
   const T* Ap = static_cast<const T*>(p.A);
   const T* A2p = static_cast<const T*>(p.A2);
   const int64_t boff = (MODE == Mode::Rows) ? (int64_t)e * p.b_estride : 0;
   const T* Bp = static_cast<const T*>(p.B) + boff;
   const T* B2p = (DUAL || KCAT) ? static_cast<const T*>(p.B2) + boff : nullptr;
   const int nk = (k_len + BK - 1) / BK;
-  const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+  constexpr int64_t TS = sizeof(T);
+  // Per-tile resources: every offset below is relative to the tile's first
+  // row / column and stays far below 2^31.
+  rsrc_t rA, rA2, rB, rB2;
+  if constexpr (A_K) {
+    const int64_t rows = (int64_t)min(row_end - m0, BM);
+    rA = make_rsrc(Ap + (int64_t)m0 * p.lda, rows * p.lda * TS);
+    rA2 = make_rsrc(KCAT ? A2p + (int64_t)m0 * p.lda : Ap, KCAT ? rows * p.lda * TS : 0);
+  } else {
+    rA = make_rsrc(Ap + k_begin * p.lda + m0, (int64_t)k_len * p.lda * TS);
+    rA2 = rA;
+  }
+  if constexpr (B_K) {
+    rB = make_rsrc(Bp + (int64_t)n0 * p.ldb, (int64_t)BN * p.ldb * TS);
+    rB2 = make_rsrc(B2p ? B2p + (int64_t)n0 * p.ldb : Bp, B2p ? (int64_t)BN * p.ldb * TS : 0);
+  } else if constexpr (MODE == Mode::Expert) {
+    rB = make_rsrc(Bp + k_begin * p.ldb + n0, (int64_t)k_len * p.ldb * TS);
+    rB2 = make_rsrc(B2p ? B2p + k_begin * p.ldb + n0 : Bp, B2p ? (int64_t)k_len * p.ldb * TS : 0);
+  } else {
+    rB = make_rsrc(Bp + n0, (int64_t)p.K * p.ldb * TS);
+    rB2 = make_rsrc(B2p ? B2p + n0 : Bp, B2p ? (int64_t)p.K * p.ldb * TS : 0);
+  }
+  // N-major B of a DUAL tile: per-group base and size, for resources built
+  // from a wave-uniform pointer inside the load loop
+  const T* bt0 = (MODE == Mode::Expert) ? Bp + k_begin * p.ldb + n0 : Bp + n0;
+  const T* bt1 = B2p ? ((MODE == Mode::Expert) ? B2p + k_begin * p.ldb + n0 : B2p + n0) : bt0;
+  const int64_t bbytes = (MODE == Mode::Expert ? (int64_t)k_len : (int64_t)p.K) * p.ldb * TS;
 
-  u32x4_t ra[A_REGS];
-  u32x4_t rb[B_REGS];
+  u32x4_t ra0[A_REGS], rb0[B_REGS];
+  u32x4_t ra1[STAGES > 1 ? A_REGS : 1], rb1[STAGES > 1 ? B_REGS : 1];
   f32x4_t acc[NB][FM][FN];
 #pragma unroll
   for (int g = 0; g < NB; ++g)
@@ -166,26 +227,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[g][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto load = [&](int kt) __attribute__((always_inline)) {
+  auto load = [&](int kt, auto& ra, auto& rb) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     // ---- A
     if constexpr (A_K) {
-      const T* src = Ap;
+      bool second = false;
       int kk = k0;
       if constexpr (KCAT) {
-        if (k0 >= p.Kseg) {
-          src = A2p;
-          kk = k0 - p.Kseg;
-        }
+        second = k0 >= p.Kseg;
+        kk = second ? k0 - p.Kseg : k0;
       }
 #pragma unroll
       for (int u = 0; u < A_UNITS; ++u) {
         const int lin = tid + u * kThreads;
         const int m = lin >> 3, c = lin & 7;
-        const int row = m0 + m;
-        ra[u] = row < row_end
-                    ? *reinterpret_cast<const u32x4_t*>(src + (int64_t)row * p.lda + kk + c * EPC)
-                    : zero;
+        const uint32_t off = (uint32_t)((m * p.lda + kk + c * EPC) * TS);
+        ra[u] = bload(second ? rA2 : rA, off);  // rows past the segment read zero
       }
     } else {
 #pragma unroll
@@ -195,31 +252,28 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
 #pragma unroll
         for (int q = 0; q < EPC; ++q) {
           const int kr = k0 + kb * EPC + q;
-          ra[u * EPC + q] =
-              (blk < A_BLK && kr < k_len)
-                  ? *reinterpret_cast<const u32x4_t*>(Ap + (k_begin + kr) * p.lda + m0 + mb * EPC)
-                  : zero;
+          uint32_t off = (uint32_t)((kr * p.lda + mb * EPC) * TS);
+          if constexpr (A_BLK % kThreads != 0) off = blk < A_BLK ? off : kOob;
+          ra[u * EPC + q] = bload(rA, off);  // rows past k_len read zero
         }
       }
     }
     // ---- B
     if constexpr (B_K) {
-      const T* s1 = Bp;
+      bool second = false;
       int kk = k0;
       if constexpr (KCAT) {
-        if (k0 >= p.Kseg) {
-          s1 = B2p;
-          kk = k0 - p.Kseg;
-        }
+        second = k0 >= p.Kseg;
+        kk = second ? k0 - p.Kseg : k0;
       }
 #pragma unroll
       for (int u = 0; u < B_UNITS; ++u) {
         const int lin = tid + u * kThreads;
         const int n = lin >> 3, c = lin & 7;
-        const int g = n / BN;
+        const int g = DUAL ? n / BN : 0;
         const int nin = n - g * BN;
-        const T* src = (DUAL && g) ? B2p : s1;
-        rb[u] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(n0 + nin) * p.ldb + kk + c * EPC);
+        const uint32_t off = (uint32_t)((nin * p.ldb + kk + c * EPC) * TS);
+        rb[u] = bload(((DUAL && g) || second) ? rB2 : rB, off);
       }
     } else {
 #pragma unroll
@@ -227,23 +281,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
         const int blk = tid + u * kThreads;
         const int kb = blk & 7, nb = blk >> 3;
         const int ncol = nb * EPC;
-        const int g = ncol / BN;
+        // each operand group spans whole waves (static_assert above), so the
+        // group, and with it the resource, is wave-uniform
+        const int g = DUAL ? ncol / BN : 0;
         const int nin = ncol - g * BN;
-        const T* src = (DUAL && g) ? B2p : Bp;
-        const int gc = n0 + nin;
-        const bool colok = blk < B_BLK && (MODE != Mode::Dense || gc < p.N);
+        rsrc_t r = rB;
+        if constexpr (DUAL) r = make_rsrc(wave_uniform(g ? bt1 : bt0), bbytes);
+        bool colok = true;
+        if constexpr (B_BLK % kThreads != 0) colok = blk < B_BLK;
+        if constexpr (MODE == Mode::Dense) colok = colok && n0 + nin < p.N;
 #pragma unroll
         for (int q = 0; q < EPC; ++q) {
           const int kr = k0 + kb * EPC + q;
-          const bool ok = colok && (MODE != Mode::Expert || kr < k_len);
-          rb[u * EPC + q] =
-              ok ? *reinterpret_cast<const u32x4_t*>(src + (k_begin + kr) * p.ldb + gc) : zero;
+          const uint32_t off = colok ? (uint32_t)((kr * p.ldb + nin) * TS) : kOob;
+          rb[u * EPC + q] = bload(r, off);
         }
       }
     }
   };
 
-  auto store = [&](int buf) __attribute__((always_inline)) {
+  auto store = [&](int buf, const auto& ra, const auto& rb) __attribute__((always_inline)) {
     if constexpr (A_K) {
 #pragma unroll
       for (int u = 0; u < A_UNITS; ++u) {
@@ -255,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
 #pragma unroll
       for (int u = 0; u < A_UNITS; ++u) {
         const int blk = tid + u * kThreads;
-        if (blk < A_BLK) {
+        if (A_BLK % kThreads == 0 || blk < A_BLK) {
           const int kb = blk & 7, mb = blk >> 3;
           u32x4_t t[EPC];
           transpose_block(&ra[u * EPC], t, T());
@@ -278,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
 #pragma unroll
       for (int u = 0; u < B_UNITS; ++u) {
         const int blk = tid + u * kThreads;
-        if (blk < B_BLK) {
+        if (B_BLK % kThreads == 0 || blk < B_BLK) {
           const int kb = blk & 7, nb = blk >> 3;
           u32x4_t t[EPC];
           transpose_block(&rb[u * EPC], t, T());
@@ -322,15 +379,39 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
     }
   };
 
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
-    compute(cur);
-    if (kt + 1 < nk) store(cur ^ 1);
+  if constexpr (STAGES == 1) {
+    // two LDS stages fed from one register stage: the loads of tile t+1 are
+    // in flight while the MFMAs consume tile t
+    load(0, ra0, rb0);
+    store(0, ra0, rb0);
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) load(kt + 1, ra0, rb0);
+      compute(cur);
+      if (kt + 1 < nk) store(cur ^ 1, ra0, rb0);
+      __syncthreads();
+    }
+  } else {
+    // two LDS stages fed from two register stages (tiles t+1 and t+2 in
+    // flight), unrolled by two so each register set is named statically;
+    // prefetches past the last tile reload it (clamped) instead of branching
+    const int last = nk - 1;
+    load(0, ra0, rb0);
+    load(min(1, last), ra1, rb1);
+    store(0, ra0, rb0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      load(min(kt + 2, last), ra0, rb0);
+      compute(0);
+      store(1, ra1, rb1);
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      load(min(kt + 3, last), ra1, rb1);
+      compute(1);
+      store(0, ra0, rb0);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: lane holds column (lane & 15), rows 4*(lane>>4) + 0..3 of
@@ -350,7 +431,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
           static_cast<T*>(p.C)[o] = Elem<T>::from_f(v0);
         } else if constexpr (EPI == Epi::SwiGLU || EPI == Epi::SwiGLUSave) {
           const float v1 = acc[NB - 1][i][j][q];
-          const float hv = v0 / (1.f + expf(-v0)) * v1;
+          // silu with the hardware exp and reciprocal (about 1 ulp each)
+          const float hv = __fdividef(v0, 1.f + __expf(-v0)) * v1;
           static_cast<T*>(p.C)[o] = Elem<T>::from_f(hv);
           if constexpr (EPI == Epi::SwiGLUSave) {
             static_cast<T*>(p.C2)[o] = Elem<T>::from_f(v0);
