@@ -57,7 +57,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="balanced_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=512,
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the batch the oracle runs for the CPU baseline")
     ap.add_argument("--stage-reps", type=int, default=5)
     args = ap.parse_args()
@@ -111,6 +111,14 @@ def main():
         return B.moe_bounded_forward(plan, X, Wr, bias, Wg, Wu, Wd, Y=Y, topk_idx=idx, gates=gates,
                                      logits=None, want_logits=False, ws=ws, stream=stream)
 
+    # a plain 256 MiB device copy, outside the timed region: the reference
+    # for scaling the HBM byte counters of a profiled run (read 256 MiB,
+    # write 256 MiB)
+    cp_src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    torch.cuda.synchronize()
+    del cp_src, cp_dst
     log(f"plan: K={K} c_eff={plan.c_eff} workspace={plan.fwd_workspace_bytes} B")
     for _ in range(args.warmup):
         stats = step()[4]

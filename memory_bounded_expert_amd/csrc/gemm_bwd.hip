@@ -44,7 +44,8 @@ hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd
   p.N = F; p.K = H;
   p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
   const int bn = pick_bn(F, true);
-  const dim3 grid((unsigned)g.grid_m, (unsigned)(F / bn));
+  p.ntiles = F / bn;
+  const dim3 grid((unsigned)(g.grid_m * p.ntiles));
   return dtype == MOE_BF16 ? dh_t<bf16_t>(p, grid, bn, st) : dh_t<float>(p, grid, bn, st);
 }
 
@@ -58,7 +59,8 @@ hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du,
   p.N = H; p.K = 2 * F; p.Kseg = F;
   p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
   const int bn = pick_bn(H, true);
-  const dim3 grid((unsigned)g.grid_m, (unsigned)(H / bn));
+  p.ntiles = H / bn;
+  const dim3 grid((unsigned)(g.grid_m * p.ntiles));
   return dtype == MOE_BF16 ? dx_t<bf16_t>(p, grid, bn, st) : dx_t<float>(p, grid, bn, st);
 }
 

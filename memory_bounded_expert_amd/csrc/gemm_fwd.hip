@@ -34,7 +34,8 @@ hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const vo
   p.N = F; p.K = H;
   p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
   const int bn = F % 128 == 0 ? 128 : 64;
-  const dim3 grid((unsigned)g.grid_m, (unsigned)(F / bn));
+  p.ntiles = F / bn;
+  const dim3 grid((unsigned)(g.grid_m * p.ntiles));
   const bool save = a != nullptr;
   return dtype == MOE_BF16 ? up_swiglu_t<bf16_t>(p, grid, bn, save, st)
                            : up_swiglu_t<float>(p, grid, bn, save, st);
@@ -50,7 +51,8 @@ hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd
   p.N = H; p.K = F;
   p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
   const int bn = pick_bn(H, true);
-  const dim3 grid((unsigned)g.grid_m, (unsigned)(H / bn));
+  p.ntiles = H / bn;
+  const dim3 grid((unsigned)(g.grid_m * p.ntiles));
   return dtype == MOE_BF16 ? down_t<bf16_t>(p, grid, bn, st) : down_t<float>(p, grid, bn, st);
 }
 

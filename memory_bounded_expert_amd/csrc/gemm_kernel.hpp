@@ -57,6 +57,7 @@ struct Params {
   int64_t ldc;
   int64_t c_estride;  // elements between experts' C (Expert mode)
   int M, N, K, Kseg;
+  int ntiles;  // Rows mode: N-tiles per M-tile (N / BN)
   const int2* tiles;
   const int32_t* tile_count;
   const int32_t* offsets;
@@ -156,12 +157,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
 
   const int tid = threadIdx.x;
   int e = 0, m0 = 0, row_end = 0;
-  const int n0 = blockIdx.y * BN;
+  int n0 = blockIdx.y * BN;
   int64_t k_begin = 0;
   int k_len = p.K;
   if constexpr (MODE == Mode::Rows) {
-    if ((int)blockIdx.x >= *p.tile_count) return;
-    const int2 tl = p.tiles[blockIdx.x];
+    // 1-D grid over (M-tile, N-tile) pairs, sized for the worst case; the
+    // chunk's real M-tile count is on the device.  Hardware hands out
+    // work-group ids round-robin over the 8 XCDs (each with its own L2), so
+    // the ids are renumbered to give every XCD a contiguous run of tiles in
+    // (M-tile, N-tile) order: the work-groups an XCD runs together then share
+    // their A rows (same M-tile) and their expert's weights (neighbouring
+    // M-tiles) through that XCD's L2.
+    const int total = *p.tile_count * p.ntiles;
+    const int L = blockIdx.x;
+    if (L >= total) return;
+    const int xcd = L & 7, slot = L >> 3;
+    const int q = total >> 3, r = total & 7;
+    const int lid = xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+    const int mt = lid / p.ntiles;
+    n0 = (lid - mt * p.ntiles) * BN;
+    const int2 tl = p.tiles[mt];
     e = tl.x;
     m0 = tl.y;
     row_end = p.offsets[e + 1];
@@ -180,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
   // visible so addresses and buffer resources stay in scalar registers.
   e = __builtin_amdgcn_readfirstlane(e);
   m0 = __builtin_amdgcn_readfirstlane(m0);
+  n0 = __builtin_amdgcn_readfirstlane(n0);
   row_end = __builtin_amdgcn_readfirstlane(row_end);
   k_len = __builtin_amdgcn_readfirstlane(k_len);
   k_begin = (int64_t)__builtin_amdgcn_readfirstlane((int)k_begin);
