@@ -101,10 +101,6 @@ def main():
     Y = torch.empty((N, wl.H), dtype=dt, device=dev)
     idx = torch.empty((N, k), dtype=torch.int32, device=dev)
     gates = torch.empty((N, k), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-    mem0 = torch.cuda.memory_allocated(dev)
-    torch.cuda.reset_peak_memory_stats(dev)
-    ws = B.workspace(plan, "fwd", dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
@@ -119,6 +115,12 @@ def main():
     cp_dst.copy_(cp_src)
     torch.cuda.synchronize()
     del cp_src, cp_dst
+    torch.cuda.empty_cache()
+    # device memory the layer adds on top of its inputs and outputs: the
+    # workspace (routing plan + the bounded per-chunk buffers)
+    mem0 = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    ws = B.workspace(plan, "fwd", dev)
     log(f"plan: K={K} c_eff={plan.c_eff} workspace={plan.fwd_workspace_bytes} B")
     for _ in range(args.warmup):
         stats = step()[4]

@@ -1,11 +1,37 @@
 // Backward contractions: dY W_down^T, [da du] [W_gate W_up]^T, and the
 // per-expert weight gradients accumulated chunk by chunk.
 #include "gemm_kernel.hpp"
+#include "gemm_lds.hpp"
 
 namespace moe {
 using namespace gemm;
 
 namespace {
+hipError_t dh_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
+  if (bn == 256) return launch_lds<Mode::Rows, 128, 256, false, true, true, false, Epi::F32>(p, grid, st);
+  if (bn == 128) return launch_lds<Mode::Rows, 128, 128, false, true, true, false, Epi::F32>(p, grid, st);
+  return launch_lds<Mode::Rows, 128, 64, false, true, true, false, Epi::F32>(p, grid, st);
+}
+
+hipError_t dx_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
+  if (bn == 256) return launch_lds<Mode::Rows, 128, 256, false, true, true, true, Epi::Store>(p, grid, st);
+  if (bn == 128) return launch_lds<Mode::Rows, 128, 128, false, true, true, true, Epi::Store>(p, grid, st);
+  return launch_lds<Mode::Rows, 128, 64, false, true, true, true, Epi::Store>(p, grid, st);
+}
+
+template <int BM>
+hipError_t wgu_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
+  if (bn == 128) return launch_lds<Mode::Expert, BM, 128, true, false, false, false, Epi::AccF32>(p, grid, st);
+  return launch_lds<Mode::Expert, BM, 64, true, false, false, false, Epi::AccF32>(p, grid, st);
+}
+
+template <int BM>
+hipError_t wd_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
+  if (bn == 256) return launch_lds<Mode::Expert, BM, 256, false, false, false, false, Epi::AccF32>(p, grid, st);
+  if (bn == 128) return launch_lds<Mode::Expert, BM, 128, false, false, false, false, Epi::AccF32>(p, grid, st);
+  return launch_lds<Mode::Expert, BM, 64, false, false, false, false, Epi::AccF32>(p, grid, st);
+}
+
 template <typename T>
 hipError_t dh_t(const Params& p, dim3 grid, int bn, hipStream_t st) {
   if (bn == 256) return launch<T, Mode::Rows, 128, 256, false, true, true, false, Epi::F32>(p, grid, st);
@@ -46,7 +72,7 @@ hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd
   const int bn = pick_bn(F, true);
   p.ntiles = F / bn;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
-  return dtype == MOE_BF16 ? dh_t<bf16_t>(p, grid, bn, st) : dh_t<float>(p, grid, bn, st);
+  return dtype == MOE_BF16 ? dh_bf16(p, grid, bn, st) : dh_t<float>(p, grid, bn, st);
 }
 
 hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du, const void* Wg,
@@ -61,7 +87,7 @@ hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du,
   const int bn = pick_bn(H, true);
   p.ntiles = H / bn;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
-  return dtype == MOE_BF16 ? dx_t<bf16_t>(p, grid, bn, st) : dx_t<float>(p, grid, bn, st);
+  return dtype == MOE_BF16 ? dx_bf16(p, grid, bn, st) : dx_t<float>(p, grid, bn, st);
 }
 
 hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, const void* da,
@@ -77,7 +103,7 @@ hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, cons
   const int bn = F % 128 == 0 ? 128 : 64;
   const dim3 grid((unsigned)(H / bm), (unsigned)(F / bn), (unsigned)E);
   if (dtype == MOE_BF16)
-    return bm == 128 ? wgu_t<bf16_t, 128>(p, grid, bn, st) : wgu_t<bf16_t, 64>(p, grid, bn, st);
+    return bm == 128 ? wgu_bf16<128>(p, grid, bn, st) : wgu_bf16<64>(p, grid, bn, st);
   return bm == 128 ? wgu_t<float, 128>(p, grid, bn, st) : wgu_t<float, 64>(p, grid, bn, st);
 }
 
@@ -93,7 +119,7 @@ hipError_t gemm_wgrad_d(int dtype, const int32_t* offsets, const void* hg, const
   const int bn = pick_bn(H, true);
   const dim3 grid((unsigned)(F / bm), (unsigned)(H / bn), (unsigned)E);
   if (dtype == MOE_BF16)
-    return bm == 128 ? wd_t<bf16_t, 128>(p, grid, bn, st) : wd_t<bf16_t, 64>(p, grid, bn, st);
+    return bm == 128 ? wd_bf16<128>(p, grid, bn, st) : wd_bf16<64>(p, grid, bn, st);
   return bm == 128 ? wd_t<float, 128>(p, grid, bn, st) : wd_t<float, 64>(p, grid, bn, st);
 }
 

@@ -1,11 +1,27 @@
 // Forward contractions: router logits, expert up-projection with the fused
 // SwiGLU epilogue, expert down-projection.
 #include "gemm_kernel.hpp"
+#include "gemm_lds.hpp"
 
 namespace moe {
 using namespace gemm;
 
 namespace {
+hipError_t up_swiglu_bf16(const Params& p, dim3 grid, int bn, bool save, hipStream_t st) {
+  if (bn == 128) {
+    return save ? launch_lds<Mode::Rows, 128, 128, true, true, false, false, Epi::SwiGLUSave>(p, grid, st)
+                : launch_lds<Mode::Rows, 128, 128, true, true, false, false, Epi::SwiGLU>(p, grid, st);
+  }
+  return save ? launch_lds<Mode::Rows, 128, 64, true, true, false, false, Epi::SwiGLUSave>(p, grid, st)
+              : launch_lds<Mode::Rows, 128, 64, true, true, false, false, Epi::SwiGLU>(p, grid, st);
+}
+
+hipError_t down_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
+  if (bn == 256) return launch_lds<Mode::Rows, 128, 256, false, true, false, false, Epi::Store>(p, grid, st);
+  if (bn == 128) return launch_lds<Mode::Rows, 128, 128, false, true, false, false, Epi::Store>(p, grid, st);
+  return launch_lds<Mode::Rows, 128, 64, false, true, false, false, Epi::Store>(p, grid, st);
+}
+
 template <typename T>
 hipError_t up_swiglu_t(const Params& p, dim3 grid, int bn, bool save, hipStream_t st) {
   if (bn == 128) {
@@ -37,7 +53,7 @@ hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const vo
   p.ntiles = F / bn;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
   const bool save = a != nullptr;
-  return dtype == MOE_BF16 ? up_swiglu_t<bf16_t>(p, grid, bn, save, st)
+  return dtype == MOE_BF16 ? up_swiglu_bf16(p, grid, bn, save, st)
                            : up_swiglu_t<float>(p, grid, bn, save, st);
 }
 
@@ -53,7 +69,7 @@ hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd
   const int bn = pick_bn(H, true);
   p.ntiles = H / bn;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
-  return dtype == MOE_BF16 ? down_t<bf16_t>(p, grid, bn, st) : down_t<float>(p, grid, bn, st);
+  return dtype == MOE_BF16 ? down_bf16(p, grid, bn, st) : down_t<float>(p, grid, bn, st);
 }
 
 hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bias, float* logits,
@@ -67,7 +83,7 @@ hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bi
   p.bias = bias;
   const dim3 grid((unsigned)ceil_div(N, 128), (unsigned)ceil_div(E, 64));
   return dtype == MOE_BF16
-             ? launch<bf16_t, Mode::Dense, 128, 64, false, true, false, false, Epi::BiasF32>(p, grid, st)
+             ? launch_lds<Mode::Dense, 128, 64, false, true, false, false, Epi::BiasF32>(p, grid, st)
              : launch<float, Mode::Dense, 128, 64, false, true, false, false, Epi::BiasF32>(p, grid, st);
 }
 

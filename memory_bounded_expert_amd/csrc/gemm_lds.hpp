@@ -1,0 +1,398 @@
+// bf16 grouped GEMM on gfx950 with an LDS-only operand pipeline.
+//
+// Same contraction modes as gemm_kernel.hpp (Rows: expert segments of a
+// chunk, M-tiles from the planner's device-side list; Dense: router; Expert:
+// weight gradients), same 2 x 2 wave grid of v_mfma_f32_16x16x32_bf16 with
+// fp32 accumulation, and the same K order for every output element -- so a
+// row's result does not depend on which rows share its tile.  What changes
+// is how operands reach the MFMAs:
+//
+//  * Every operand tile goes from HBM straight into LDS with buffer loads
+//    that write LDS (16 bytes per lane; lane L of a wave lands at base +
+//    16 L).  No staging registers, so NS = 3..4 LDS stages fit and two to
+//    three K-tiles are in flight per work-group while the MFMAs consume the
+//    current one.  Loads past a tile's valid rows (buffer resource bounds)
+//    write zeros.
+//  * K-contiguous operands (activation rows; weights in the transposed
+//    products) are stored as rows of 8 chunks of 16 bytes, chunk c of row r
+//    at slot c ^ (r & 7), and read with ds_read_b128.
+//  * M/N-contiguous operands (weights in the forward products; activations
+//    in the weight gradients) stay M/N-contiguous in LDS and are read with
+//    ds_read_b64_tr_b16: in each 16-lane group, lanes 4j..4j+3 address row j
+//    and lane i receives column i of rows 0..3, so two reads give a lane the
+//    8 consecutive k of one column that the MFMA operand needs.  Chunk c of
+//    row k sits at c ^ sw(k); sw makes the 32 lanes of each half-wave hit 64
+//    distinct banks.
+//
+// The global-side permutation that realises each swizzle is applied in the
+// per-lane load offsets, so the LDS writes of a wave stay one contiguous KiB.
+#pragma once
+
+#include "device_common.hpp"
+#include "gemm_kernel.hpp"  // Mode, Epi, Params, make_rsrc, wave_uniform
+#include "moe_internal.h"
+
+namespace moe {
+namespace gemm {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_p;
+typedef __attribute__((address_space(3))) void* lds_void_p;
+
+constexpr int kLdsBytes = 160 * 1024;
+
+// swizzle of a row of RC 16-byte chunks read with the transposing loads
+template <int RC>
+__device__ __forceinline__ int trswz(int k) {
+  if constexpr (RC >= 16) return 2 * ((k & 3) | (((k >> 3) & 1) << 2));
+  else return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1));
+}
+
+// Buffer resource as four scalar dwords, for the inline-asm loads below.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_srd(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const int n = (int)(bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes));
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(n);
+  r.w = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from a buffer straight into LDS at lds + 16 * lane.
+// Written as inline asm on purpose: the compiler cannot tell that the LDS
+// reads of the stage being computed do not alias the stages being filled, and
+// would otherwise drain every load (vmcnt(0)) before each LDS read.  The
+// pipeline does its own vmcnt accounting; no compiler-visible vector memory
+// operation is outstanding while these are in flight.
+__device__ __forceinline__ void lds_load16(const i32x4_t& srd, void* lds, uint32_t voff) {
+  const uint32_t m0v =
+      __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_void_p)lds));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(srd)
+               : "memory", "m0");
+}
+
+// Work-group barrier for the LDS pipeline: waits for this wave's LDS reads
+// only (outstanding global->LDS loads stay in flight across it).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <Mode MODE, int BM, int BN, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
+struct LdsCfg {
+  static constexpr int BK = 64;               // bf16 per K-tile
+  static constexpr int NB = DUAL ? 2 : 1;
+  static constexpr int NCOL = BN * NB;
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = NCOL * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int NS = (kLdsBytes / STAGE) > 4 ? 4 : (kLdsBytes / STAGE);
+  // wave-instructions (1 KiB each) per tile, and per wave
+  static constexpr int A_INSTR = A_BYTES / 1024;
+  static constexpr int B_INSTR = B_BYTES / 1024;
+  static constexpr int A_PW = A_INSTR / 4;
+  static constexpr int B_PW = B_INSTR / 4;
+  static constexpr int PER_TILE = A_PW + B_PW;  // loads per thread per K-tile
+  static_assert(A_INSTR % 4 == 0 && B_INSTR % 4 == 0, "tile must split over 4 waves");
+  static_assert(NS >= 3, "need at least three LDS stages");
+};
+
+template <Mode MODE, int BM, int BN, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
+__global__ __launch_bounds__(kThreads) void gemm_lds_kernel(const Params p) {
+  using C = LdsCfg<MODE, BM, BN, DUAL, A_K, B_K, KCAT, EPI>;
+  using T = bf16_t;
+  constexpr int BK = C::BK, NB = C::NB, NS = C::NS;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int RCA = BM / 8;  // chunks per LDS row of an M-contiguous A tile
+  constexpr int RCB = BN / 8;  // chunks per LDS row of an N-contiguous B group
+  static_assert(!(DUAL && KCAT), "DUAL and KCAT are exclusive");
+  static_assert(!(DUAL && B_K), "DUAL needs an N-contiguous B");
+  static_assert(A_K || RCA >= 8, "M-contiguous A needs BM >= 64");
+  static_assert(B_K || RCB >= 8, "N-contiguous B needs BN >= 64");
+
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  // wave index in a scalar register: LDS destinations (M0) and operand-group
+  // resources derive from it
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int e = 0, m0 = 0, row_end = 0;
+  int n0 = blockIdx.y * BN;
+  int64_t k_begin = 0;
+  int k_len = p.K;
+  if constexpr (MODE == Mode::Rows) {
+    // XCD-aware renumbering of the 1-D grid (see gemm_kernel.hpp)
+    const int total = *p.tile_count * p.ntiles;
+    const int L = blockIdx.x;
+    if (L >= total) return;
+    const int xcd = L & 7, slot = L >> 3;
+    const int q = total >> 3, r = total & 7;
+    const int lid = xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+    const int mt = lid / p.ntiles;
+    n0 = (lid - mt * p.ntiles) * BN;
+    const int2 tl = p.tiles[mt];
+    e = tl.x;
+    m0 = tl.y;
+    row_end = p.offsets[e + 1];
+  } else if constexpr (MODE == Mode::Dense) {
+    m0 = blockIdx.x * BM;
+    row_end = p.M;
+  } else {
+    e = blockIdx.z;
+    k_begin = p.offsets[e];
+    k_len = p.offsets[e + 1] - (int)k_begin;
+    if (k_len <= 0) return;
+    m0 = blockIdx.x * BM;
+    row_end = p.M;
+  }
+  e = __builtin_amdgcn_readfirstlane(e);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  n0 = __builtin_amdgcn_readfirstlane(n0);
+  row_end = __builtin_amdgcn_readfirstlane(row_end);
+  k_len = __builtin_amdgcn_readfirstlane(k_len);
+  k_begin = (int64_t)__builtin_amdgcn_readfirstlane((int)k_begin);
+
+  const T* Ap = static_cast<const T*>(p.A);
+  const T* A2p = static_cast<const T*>(p.A2);
+  const int64_t boff = (MODE == Mode::Rows) ? (int64_t)e * p.b_estride : 0;
+  const T* Bp = static_cast<const T*>(p.B) + boff;
+  const T* B2p = (DUAL || KCAT) ? static_cast<const T*>(p.B2) + boff : Bp;
+  const int nk = (k_len + BK - 1) / BK;
+  constexpr int64_t TS = 2;
+
+  // ---- per-tile buffer resources (offsets below are tile-relative)
+  i32x4_t rA, rA2, rB, rB2;
+  if constexpr (A_K) {
+    const int64_t rows = (int64_t)min(row_end - m0, BM);
+    rA = make_srd(Ap + (int64_t)m0 * p.lda, rows * p.lda * TS);
+    rA2 = KCAT ? make_srd(A2p + (int64_t)m0 * p.lda, rows * p.lda * TS) : rA;
+  } else {
+    rA = make_srd(Ap + k_begin * p.lda + m0, (int64_t)k_len * p.lda * TS);
+    rA2 = rA;
+  }
+  if constexpr (B_K) {
+    rB = make_srd(Bp + (int64_t)n0 * p.ldb, (int64_t)BN * p.ldb * TS);
+    rB2 = KCAT ? make_srd(B2p + (int64_t)n0 * p.ldb, (int64_t)BN * p.ldb * TS) : rB;
+  } else {
+    const int64_t rows = (MODE == Mode::Expert) ? (int64_t)k_len : (int64_t)p.K;
+    const int64_t kb = (MODE == Mode::Expert) ? k_begin : 0;
+    rB = make_srd(Bp + kb * p.ldb + n0, rows * p.ldb * TS);
+    rB2 = DUAL ? make_srd(B2p + kb * p.ldb + n0, rows * p.ldb * TS) : rB;
+  }
+
+  auto stage_a = [&](int s) -> unsigned char* { return smem + s * C::STAGE; };
+  auto stage_b = [&](int s) -> unsigned char* { return smem + s * C::STAGE + C::A_BYTES; };
+
+  // ---- issue the loads of K-tile kt into LDS stage s
+  auto issue = [&](int kt, int s) __attribute__((always_inline)) {
+    const int k0 = kt * BK;
+    // A
+#pragma unroll
+    for (int u = 0; u < C::A_PW; ++u) {
+      const int ins = wave * C::A_PW + u;
+      unsigned char* dst = stage_a(s) + ins * 1024;
+      if constexpr (A_K) {
+        // 8 rows x 8 chunks per instruction
+        const int row = ins * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ (row & 7);
+        bool second = false;
+        int kk = k0;
+        if constexpr (KCAT) {
+          second = k0 >= p.Kseg;
+          kk = second ? k0 - p.Kseg : k0;
+        }
+        lds_load16(second ? rA2 : rA, dst, (uint32_t)((row * p.lda + kk + c * 8) * TS));
+      } else {
+        // rows of RCA chunks; 64 / RCA rows per instruction
+        constexpr int RPI = 64 / RCA;
+        const int k = ins * RPI + lane / RCA;
+        const int c = (lane % RCA) ^ trswz<RCA>(k);
+        const int kr = k0 + k;
+        const uint32_t off = kr < k_len ? (uint32_t)((kr * p.lda + c * 8) * TS) : kOob;
+        lds_load16(rA, dst, off);
+      }
+    }
+    // B
+#pragma unroll
+    for (int u = 0; u < C::B_PW; ++u) {
+      const int ins = wave * C::B_PW + u;
+      unsigned char* dst = stage_b(s) + ins * 1024;
+      if constexpr (B_K) {
+        const int row = ins * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ (row & 7);
+        bool second = false;
+        int kk = k0;
+        if constexpr (KCAT) {
+          second = k0 >= p.Kseg;
+          kk = second ? k0 - p.Kseg : k0;
+        }
+        lds_load16(second ? rB2 : rB, dst, (uint32_t)((row * p.ldb + kk + c * 8) * TS));
+      } else {
+        // group g holds instructions [g * BK * RCB / 64, ...): wave-uniform
+        constexpr int PER_G = BK * RCB / 64;
+        constexpr int RPI = 64 / RCB;
+        const int g = ins / PER_G;
+        const int gi = ins - g * PER_G;
+        const int k = gi * RPI + lane / RCB;
+        const int c = (lane % RCB) ^ trswz<RCB>(k);
+        const int kr = k0 + k;
+        bool ok = true;
+        if constexpr (MODE == Mode::Expert) ok = kr < k_len;
+        if constexpr (MODE == Mode::Dense) ok = n0 + c * 8 < p.N;
+        const uint32_t off = ok ? (uint32_t)((kr * p.ldb + c * 8) * TS) : kOob;
+        lds_load16((DUAL && g) ? rB2 : rB, dst, off);
+      }
+    }
+  };
+
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x4_t acc[NB][FM][FN];
+#pragma unroll
+  for (int g = 0; g < NB; ++g)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[g][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // MFMA operand reads
+  const int l16 = lane & 15, lg = lane >> 4;  // column/row within a fragment, k-group
+  const int trj = l16 >> 2, trq = l16 & 3;    // transposing read: row j, segment q
+  auto read_tr = [&](const unsigned char* base, int rc_bytes, int k, int col)
+                     __attribute__((always_inline)) -> s16x4_t {
+    // col: first of the 4 columns this lane addresses (a multiple of 4)
+    const int c = col >> 3;
+    const int h = (col >> 2) & 1;
+    const int rc = rc_bytes >> 4;
+    const int sw = rc >= 16 ? trswz<16>(k) : trswz<8>(k);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_p)(base + k * rc_bytes + ((c ^ sw) << 4) + (h << 3)));
+  };
+
+  auto compute = [&](int s) __attribute__((always_inline)) {
+    const unsigned char* As = stage_a(s);
+    const unsigned char* Bs = stage_b(s);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4_t af[FM];
+      u32x4_t bv[NB][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (A_K) {
+          const int r = wm * WM + i * 16 + l16;
+          const int c = ks * 4 + lg;
+          af[i] = *reinterpret_cast<const u32x4_t*>(As + r * 128 + ((c ^ (r & 7)) << 4));
+        } else {
+          const int kb = ks * 32 + lg * 8 + trj;
+          const int col = wm * WM + i * 16 + trq * 4;
+          const s16x4_t lo = read_tr(As, RCA * 16, kb, col);
+          const s16x4_t hi = read_tr(As, RCA * 16, kb + 4, col);
+          af[i] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < NB; ++g)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (B_K) {
+            const int n = wn * WN + j * 16 + l16;
+            const int c = ks * 4 + lg;
+            bv[g][j] = *reinterpret_cast<const u32x4_t*>(Bs + n * 128 + ((c ^ (n & 7)) << 4));
+          } else {
+            const unsigned char* Bg = Bs + g * (BK * RCB * 16);
+            const int kb = ks * 32 + lg * 8 + trj;
+            const int col = wn * WN + j * 16 + trq * 4;
+            const s16x4_t lo = read_tr(Bg, RCB * 16, kb, col);
+            const s16x4_t hi = read_tr(Bg, RCB * 16, kb + 4, col);
+            bv[g][j] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        }
+#pragma unroll
+      for (int g = 0; g < NB; ++g)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) Mfma<bf16_t>::run(af[i], bv[g][j], acc[g][i][j]);
+    }
+  };
+
+  // ---- pipeline: NS stages, NS-1 tiles in flight before the first compute.
+  // Tiles past the last are re-issued as copies of the last one (clamped
+  // index) so that every iteration waits on the same count.
+  const int last = nk - 1;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(min(s, last), s);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<(NS - 2) * C::PER_TILE>();  // this thread's loads of tile kt landed
+    lds_barrier();                          // everyone's landed; stage kt-1 is free
+    issue(min(kt + NS - 1, last), (kt + NS - 1) % NS);
+    compute(kt % NS);
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue (as gemm_kernel.hpp)
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int grow = m0 + wm * WM + i * 16 + 4 * lg + q;
+        const int gcol = n0 + wn * WN + j * 16 + l16;
+        if (grow >= row_end) continue;
+        const int64_t o = (int64_t)grow * p.ldc + gcol;
+        const float v0 = acc[0][i][j][q];
+        if constexpr (EPI == Epi::Store) {
+          static_cast<T*>(p.C)[o] = f2bf(v0);
+        } else if constexpr (EPI == Epi::SwiGLU || EPI == Epi::SwiGLUSave) {
+          const float v1 = acc[NB - 1][i][j][q];
+          const float hv = __fdividef(v0, 1.f + __expf(-v0)) * v1;
+          static_cast<T*>(p.C)[o] = f2bf(hv);
+          if constexpr (EPI == Epi::SwiGLUSave) {
+            static_cast<T*>(p.C2)[o] = f2bf(v0);
+            static_cast<T*>(p.C3)[o] = f2bf(v1);
+          }
+        } else if constexpr (EPI == Epi::F32) {
+          static_cast<float*>(p.C)[o] = v0;
+        } else if constexpr (EPI == Epi::BiasF32) {
+          if (gcol < p.N) static_cast<float*>(p.C)[o] = v0 + (p.bias ? p.bias[gcol] : 0.f);
+        } else {  // AccF32
+          float* Cp = static_cast<float*>(p.C) + (int64_t)e * p.c_estride;
+          Cp[o] += v0;
+          if constexpr (DUAL) {
+            float* C2p = static_cast<float*>(p.C2) + (int64_t)e * p.c_estride;
+            C2p[o] += acc[1][i][j][q];
+          }
+        }
+      }
+}
+
+template <Mode MODE, int BM, int BN, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
+hipError_t launch_lds(const Params& p, dim3 grid, hipStream_t st) {
+  using C = LdsCfg<MODE, BM, BN, DUAL, A_K, B_K, KCAT, EPI>;
+  auto kern = gemm_lds_kernel<MODE, BM, BN, DUAL, A_K, B_K, KCAT, EPI>;
+  const int lds = C::NS * C::STAGE;
+  static bool attr_set = false;  // per instantiation; benign race (idempotent)
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  kern<<<grid, kThreads, lds, st>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace gemm
+}  // namespace moe
