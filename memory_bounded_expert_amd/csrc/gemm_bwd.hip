@@ -8,28 +8,28 @@ using namespace gemm;
 
 namespace {
 hipError_t dh_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
-  if (bn == 256) return launch_lds<Mode::Rows, 128, 256, false, true, true, false, Epi::F32>(p, grid, st);
-  if (bn == 128) return launch_lds<Mode::Rows, 128, 128, false, true, true, false, Epi::F32>(p, grid, st);
-  return launch_lds<Mode::Rows, 128, 64, false, true, true, false, Epi::F32>(p, grid, st);
+  if (bn == 256) return launch_lds<Mode::Rows, Shape<128, 256, 2, 4, 64, 1>, false, true, true, false, Epi::F32>(p, grid, st);
+  if (bn == 128) return launch_lds<Mode::Rows, Shape<128, 128, 2, 4, 64, 1>, false, true, true, false, Epi::F32>(p, grid, st);
+  return launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, false, true, true, false, Epi::F32>(p, grid, st);
 }
 
 hipError_t dx_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
-  if (bn == 256) return launch_lds<Mode::Rows, 128, 256, false, true, true, true, Epi::Store>(p, grid, st);
-  if (bn == 128) return launch_lds<Mode::Rows, 128, 128, false, true, true, true, Epi::Store>(p, grid, st);
-  return launch_lds<Mode::Rows, 128, 64, false, true, true, true, Epi::Store>(p, grid, st);
+  if (bn == 256) return launch_lds<Mode::Rows, Shape<128, 256, 2, 4, 64, 1>, false, true, true, true, Epi::Store>(p, grid, st);
+  if (bn == 128) return launch_lds<Mode::Rows, Shape<128, 128, 2, 4, 64, 1>, false, true, true, true, Epi::Store>(p, grid, st);
+  return launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, false, true, true, true, Epi::Store>(p, grid, st);
 }
 
 template <int BM>
 hipError_t wgu_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
-  if (bn == 128) return launch_lds<Mode::Expert, BM, 128, true, false, false, false, Epi::AccF32>(p, grid, st);
-  return launch_lds<Mode::Expert, BM, 64, true, false, false, false, Epi::AccF32>(p, grid, st);
+  if (bn == 128) return launch_lds<Mode::Expert, Shape<BM, 128, 2, 4, 64, 1>, true, false, false, false, Epi::AccF32>(p, grid, st);
+  return launch_lds<Mode::Expert, Shape<BM, 64, 2, 4, 64, 1>, true, false, false, false, Epi::AccF32>(p, grid, st);
 }
 
 template <int BM>
 hipError_t wd_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
-  if (bn == 256) return launch_lds<Mode::Expert, BM, 256, false, false, false, false, Epi::AccF32>(p, grid, st);
-  if (bn == 128) return launch_lds<Mode::Expert, BM, 128, false, false, false, false, Epi::AccF32>(p, grid, st);
-  return launch_lds<Mode::Expert, BM, 64, false, false, false, false, Epi::AccF32>(p, grid, st);
+  if (bn == 256) return launch_lds<Mode::Expert, Shape<BM, 256, 2, 4, 64, 1>, false, false, false, false, Epi::AccF32>(p, grid, st);
+  if (bn == 128) return launch_lds<Mode::Expert, Shape<BM, 128, 2, 4, 64, 1>, false, false, false, false, Epi::AccF32>(p, grid, st);
+  return launch_lds<Mode::Expert, Shape<BM, 64, 2, 4, 64, 1>, false, false, false, false, Epi::AccF32>(p, grid, st);
 }
 
 template <typename T>

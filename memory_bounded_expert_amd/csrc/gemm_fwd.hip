@@ -9,17 +9,17 @@ using namespace gemm;
 namespace {
 hipError_t up_swiglu_bf16(const Params& p, dim3 grid, int bn, bool save, hipStream_t st) {
   if (bn == 128) {
-    return save ? launch_lds<Mode::Rows, 128, 128, true, true, false, false, Epi::SwiGLUSave>(p, grid, st)
-                : launch_lds<Mode::Rows, 128, 128, true, true, false, false, Epi::SwiGLU>(p, grid, st);
+    return save ? launch_lds<Mode::Rows, Shape<128, 128, 2, 4, 64, 1>, true, true, false, false, Epi::SwiGLUSave>(p, grid, st)
+                : launch_lds<Mode::Rows, Shape<128, 128, 2, 4, 64, 1>, true, true, false, false, Epi::SwiGLU>(p, grid, st);
   }
-  return save ? launch_lds<Mode::Rows, 128, 64, true, true, false, false, Epi::SwiGLUSave>(p, grid, st)
-              : launch_lds<Mode::Rows, 128, 64, true, true, false, false, Epi::SwiGLU>(p, grid, st);
+  return save ? launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, true, true, false, false, Epi::SwiGLUSave>(p, grid, st)
+              : launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, true, true, false, false, Epi::SwiGLU>(p, grid, st);
 }
 
 hipError_t down_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
-  if (bn == 256) return launch_lds<Mode::Rows, 128, 256, false, true, false, false, Epi::Store>(p, grid, st);
-  if (bn == 128) return launch_lds<Mode::Rows, 128, 128, false, true, false, false, Epi::Store>(p, grid, st);
-  return launch_lds<Mode::Rows, 128, 64, false, true, false, false, Epi::Store>(p, grid, st);
+  if (bn == 256) return launch_lds<Mode::Rows, Shape<128, 256, 2, 4, 64, 1>, false, true, false, false, Epi::Store>(p, grid, st);
+  if (bn == 128) return launch_lds<Mode::Rows, Shape<128, 128, 2, 4, 64, 1>, false, true, false, false, Epi::Store>(p, grid, st);
+  return launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, false, true, false, false, Epi::Store>(p, grid, st);
 }
 
 template <typename T>
@@ -83,7 +83,7 @@ hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bi
   p.bias = bias;
   const dim3 grid((unsigned)ceil_div(N, 128), (unsigned)ceil_div(E, 64));
   return dtype == MOE_BF16
-             ? launch_lds<Mode::Dense, 128, 64, false, true, false, false, Epi::BiasF32>(p, grid, st)
+             ? launch_lds<Mode::Dense, Shape<128, 64, 2, 4, 64, 1>, false, true, false, false, Epi::BiasF32>(p, grid, st)
              : launch<float, Mode::Dense, 128, 64, false, true, false, false, Epi::BiasF32>(p, grid, st);
 }
 

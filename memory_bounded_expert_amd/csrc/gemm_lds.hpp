@@ -89,34 +89,62 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <Mode MODE, int BM, int BN, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
+// Work-group shape: BM x BN output tile (BN per operand group), WGM x WGN
+// waves each owning a (BM/WGM) x (BN/WGN) block, K-tiles of BK, and the number
+// of work-groups meant to share a CU (its LDS is split between them).
+template <int BM_, int BN_, int WGM_, int WGN_, int BK_, int WG_PER_CU_>
+struct Shape {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_;
+  static constexpr int WG_PER_CU = WG_PER_CU_;
+};
+// streaming shape: 8 waves of 64 x 64, BK 64, one work-group per CU
+template <int BN> using Stream = Shape<128, BN, 2, 4, 64, 1>;
+// compute shape: 2 waves of 128 x 128, BK 32, two work-groups per CU
+template <int BN> using Compute = Shape<128, BN, 1, 2, 32, 2>;
+
+template <class S, bool DUAL>
 struct LdsCfg {
-  static constexpr int BK = 64;               // bf16 per K-tile
+  static constexpr int BM = S::BM, BN = S::BN, BK = S::BK;
   static constexpr int NB = DUAL ? 2 : 1;
   static constexpr int NCOL = BN * NB;
+  static constexpr int CK = BK / 8;  // 16-byte chunks per K-contiguous LDS row
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = NCOL * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int NS = (kLdsBytes / STAGE) > 4 ? 4 : (kLdsBytes / STAGE);
+  static constexpr int BUDGET = kLdsBytes / S::WG_PER_CU;
+  static constexpr int NS = (BUDGET / STAGE) > 4 ? 4 : (BUDGET / STAGE);
+  static constexpr int WAVES = S::WGM * S::WGN;
+  static constexpr int THREADS = 64 * WAVES;
   // wave-instructions (1 KiB each) per tile, and per wave
   static constexpr int A_INSTR = A_BYTES / 1024;
   static constexpr int B_INSTR = B_BYTES / 1024;
-  static constexpr int A_PW = A_INSTR / 4;
-  static constexpr int B_PW = B_INSTR / 4;
+  static constexpr int A_PW = A_INSTR / WAVES;
+  static constexpr int B_PW = B_INSTR / WAVES;
   static constexpr int PER_TILE = A_PW + B_PW;  // loads per thread per K-tile
-  static_assert(A_INSTR % 4 == 0 && B_INSTR % 4 == 0, "tile must split over 4 waves");
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(A_INSTR % WAVES == 0 && B_INSTR % WAVES == 0, "tile must split over the waves");
   static_assert(NS >= 3, "need at least three LDS stages");
 };
 
-template <Mode MODE, int BM, int BN, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
-__global__ __launch_bounds__(kThreads) void gemm_lds_kernel(const Params p) {
-  using C = LdsCfg<MODE, BM, BN, DUAL, A_K, B_K, KCAT, EPI>;
+// swizzle of a K-contiguous row of CK chunks (conflict-free ds_read_b128 of
+// 16 rows x one chunk)
+template <int CK>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (CK == 8) return r & 7;
+  else return (r >> 2) & 3;
+}
+
+template <Mode MODE, class S, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
+__global__ __launch_bounds__(64 * S::WGM * S::WGN) void gemm_lds_kernel(const Params p) {
+  using C = LdsCfg<S, DUAL>;
   using T = bf16_t;
-  constexpr int BK = C::BK, NB = C::NB, NS = C::NS;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int BM = S::BM, BN = S::BN, BK = S::BK, NB = C::NB, NS = C::NS, CK = C::CK;
+  constexpr int WM = BM / S::WGM, WN = BN / S::WGN;
   constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int KS = BK / 32;  // MFMA k-steps per K-tile
   constexpr int RCA = BM / 8;  // chunks per LDS row of an M-contiguous A tile
   constexpr int RCB = BN / 8;  // chunks per LDS row of an N-contiguous B group
+  static_assert(FM >= 1 && FN >= 1, "wave tile too small");
   static_assert(!(DUAL && KCAT), "DUAL and KCAT are exclusive");
   static_assert(!(DUAL && B_K), "DUAL needs an N-contiguous B");
   static_assert(A_K || RCA >= 8, "M-contiguous A needs BM >= 64");
@@ -198,24 +226,23 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(const Params p) {
   // ---- issue the loads of K-tile kt into LDS stage s
   auto issue = [&](int kt, int s) __attribute__((always_inline)) {
     const int k0 = kt * BK;
+    bool second = false;  // K segment of a KCAT product (uniform)
+    int kk = k0;
+    if constexpr (KCAT) {
+      second = k0 >= p.Kseg;
+      kk = second ? k0 - p.Kseg : k0;
+    }
+    constexpr int RPIK = 64 / CK;  // K-contiguous rows per instruction
     // A
 #pragma unroll
     for (int u = 0; u < C::A_PW; ++u) {
       const int ins = wave * C::A_PW + u;
       unsigned char* dst = stage_a(s) + ins * 1024;
       if constexpr (A_K) {
-        // 8 rows x 8 chunks per instruction
-        const int row = ins * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ (row & 7);
-        bool second = false;
-        int kk = k0;
-        if constexpr (KCAT) {
-          second = k0 >= p.Kseg;
-          kk = second ? k0 - p.Kseg : k0;
-        }
+        const int row = ins * RPIK + lane / CK;
+        const int c = (lane % CK) ^ kswz<CK>(row);
         lds_load16(second ? rA2 : rA, dst, (uint32_t)((row * p.lda + kk + c * 8) * TS));
       } else {
-        // rows of RCA chunks; 64 / RCA rows per instruction
         constexpr int RPI = 64 / RCA;
         const int k = ins * RPI + lane / RCA;
         const int c = (lane % RCA) ^ trswz<RCA>(k);
@@ -230,17 +257,11 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(const Params p) {
       const int ins = wave * C::B_PW + u;
       unsigned char* dst = stage_b(s) + ins * 1024;
       if constexpr (B_K) {
-        const int row = ins * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ (row & 7);
-        bool second = false;
-        int kk = k0;
-        if constexpr (KCAT) {
-          second = k0 >= p.Kseg;
-          kk = second ? k0 - p.Kseg : k0;
-        }
+        const int row = ins * RPIK + lane / CK;
+        const int c = (lane % CK) ^ kswz<CK>(row);
         lds_load16(second ? rB2 : rB, dst, (uint32_t)((row * p.ldb + kk + c * 8) * TS));
       } else {
-        // group g holds instructions [g * BK * RCB / 64, ...): wave-uniform
+        // group g holds instructions [g * PER_G, (g + 1) * PER_G): wave-uniform
         constexpr int PER_G = BK * RCB / 64;
         constexpr int RPI = 64 / RCB;
         const int g = ins / PER_G;
@@ -257,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(const Params p) {
     }
   };
 
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % S::WGM, wn = wave / S::WGM;
   f32x4_t acc[NB][FM][FN];
 #pragma unroll
   for (int g = 0; g < NB; ++g)
@@ -274,8 +295,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(const Params p) {
     // col: first of the 4 columns this lane addresses (a multiple of 4)
     const int c = col >> 3;
     const int h = (col >> 2) & 1;
-    const int rc = rc_bytes >> 4;
-    const int sw = rc >= 16 ? trswz<16>(k) : trswz<8>(k);
+    const int sw = (rc_bytes >> 4) >= 16 ? trswz<16>(k) : trswz<8>(k);
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s16x4_p)(base + k * rc_bytes + ((c ^ sw) << 4) + (h << 3)));
   };
@@ -284,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(const Params p) {
     const unsigned char* As = stage_a(s);
     const unsigned char* Bs = stage_b(s);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       u32x4_t af[FM];
       u32x4_t bv[NB][FN];
 #pragma unroll
@@ -292,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(const Params p) {
         if constexpr (A_K) {
           const int r = wm * WM + i * 16 + l16;
           const int c = ks * 4 + lg;
-          af[i] = *reinterpret_cast<const u32x4_t*>(As + r * 128 + ((c ^ (r & 7)) << 4));
+          af[i] = *reinterpret_cast<const u32x4_t*>(As + r * (CK * 16) + ((c ^ kswz<CK>(r)) << 4));
         } else {
           const int kb = ks * 32 + lg * 8 + trj;
           const int col = wm * WM + i * 16 + trq * 4;
@@ -308,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(const Params p) {
           if constexpr (B_K) {
             const int n = wn * WN + j * 16 + l16;
             const int c = ks * 4 + lg;
-            bv[g][j] = *reinterpret_cast<const u32x4_t*>(Bs + n * 128 + ((c ^ (n & 7)) << 4));
+            bv[g][j] = *reinterpret_cast<const u32x4_t*>(Bs + n * (CK * 16) + ((c ^ kswz<CK>(n)) << 4));
           } else {
             const unsigned char* Bg = Bs + g * (BK * RCB * 16);
             const int kb = ks * 32 + lg * 8 + trj;
@@ -378,10 +398,10 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(const Params p) {
       }
 }
 
-template <Mode MODE, int BM, int BN, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
+template <Mode MODE, class S, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
 hipError_t launch_lds(const Params& p, dim3 grid, hipStream_t st) {
-  using C = LdsCfg<MODE, BM, BN, DUAL, A_K, B_K, KCAT, EPI>;
-  auto kern = gemm_lds_kernel<MODE, BM, BN, DUAL, A_K, B_K, KCAT, EPI>;
+  using C = LdsCfg<S, DUAL>;
+  auto kern = gemm_lds_kernel<MODE, S, DUAL, A_K, B_K, KCAT, EPI>;
   const int lds = C::NS * C::STAGE;
   static bool attr_set = false;  // per instantiation; benign race (idempotent)
   if (!attr_set) {
@@ -390,7 +410,7 @@ hipError_t launch_lds(const Params& p, dim3 grid, hipStream_t st) {
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  kern<<<grid, kThreads, lds, st>>>(p);
+  kern<<<grid, C::THREADS, lds, st>>>(p);
   return hipGetLastError();
 }
 
