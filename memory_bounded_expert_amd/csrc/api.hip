@@ -34,7 +34,8 @@ Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_d
   const size_t b = (size_t)elem_bytes(p.dtype);
   if (N == 0) return L;
   L.nblk = ceil_div((int64_t)ce, kPlanBlock);
-  L.max_tiles = max_row_tiles((int64_t)(k * ce), (int)E);
+  L.row_tile = row_tile_for(p);
+  L.max_tiles = max_row_tiles((int64_t)(k * ce), (int)E, L.row_tile);
   if (pass == Pass::Forward && need_logits) L.logits = take(N * E * 4);
   L.rank = take(N * k * 4);
   L.blk = take(K * (size_t)L.nblk * E * 4);
@@ -76,6 +77,7 @@ PlanBuffers plan_buffers(char* ws, const Layout& L, int32_t* offsets, int32_t* p
   b.pos = pos ? pos : (int32_t*)(ws + L.pos);
   b.nblk = L.nblk;
   b.max_tiles = L.max_tiles;
+  b.row_tile = L.row_tile;
   return b;
 }
 
@@ -84,7 +86,8 @@ RowsGeom rows_geom(const PlanBuffers& b, const moe_plan_t& P, int i, int64_t R) 
   g.tiles = b.tiles + (int64_t)i * b.max_tiles;
   g.tile_count = b.tile_count + i;
   g.offsets = b.offsets + (int64_t)i * (P.E + 1);
-  g.grid_m = max_row_tiles(R, P.E);
+  g.grid_m = max_row_tiles(R, P.E, b.row_tile);
+  g.row_tile = b.row_tile;
   return g;
 }
 

@@ -7,13 +7,27 @@ namespace moe {
 using namespace gemm;
 
 namespace {
-hipError_t dh_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
+// 256-row tiles: 4 x 2 waves of 64 x (BN/2)
+template <int BN>
+using Big = Shape<256, BN, 4, 2, 32, 1>;
+
+hipError_t dh_bf16(const Params& p, dim3 grid, int bn, int rt, hipStream_t st) {
+  if (rt == kRowTileLarge) {
+    if (bn == 256) return launch_lds<Mode::Rows, Big<256>, false, true, true, false, Epi::F32>(p, grid, st);
+    if (bn == 128) return launch_lds<Mode::Rows, Big<128>, false, true, true, false, Epi::F32>(p, grid, st);
+    return hipErrorInvalidValue;
+  }
   if (bn == 256) return launch_lds<Mode::Rows, Shape<128, 256, 2, 4, 64, 1>, false, true, true, false, Epi::F32>(p, grid, st);
   if (bn == 128) return launch_lds<Mode::Rows, Shape<128, 128, 2, 4, 64, 1>, false, true, true, false, Epi::F32>(p, grid, st);
   return launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, false, true, true, false, Epi::F32>(p, grid, st);
 }
 
-hipError_t dx_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
+hipError_t dx_bf16(const Params& p, dim3 grid, int bn, int rt, hipStream_t st) {
+  if (rt == kRowTileLarge) {
+    if (bn == 256) return launch_lds<Mode::Rows, Big<256>, false, true, true, true, Epi::Store>(p, grid, st);
+    if (bn == 128) return launch_lds<Mode::Rows, Big<128>, false, true, true, true, Epi::Store>(p, grid, st);
+    return hipErrorInvalidValue;
+  }
   if (bn == 256) return launch_lds<Mode::Rows, Shape<128, 256, 2, 4, 64, 1>, false, true, true, true, Epi::Store>(p, grid, st);
   if (bn == 128) return launch_lds<Mode::Rows, Shape<128, 128, 2, 4, 64, 1>, false, true, true, true, Epi::Store>(p, grid, st);
   return launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, false, true, true, true, Epi::Store>(p, grid, st);
@@ -69,10 +83,10 @@ hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd
   p.C = dh; p.ldc = F;
   p.N = F; p.K = H;
   p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
-  const int bn = pick_bn(F, true);
+  const int bn = g.row_tile == kRowTileLarge ? (F % 256 == 0 ? 256 : 128) : pick_bn(F, true);
   p.ntiles = F / bn;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
-  return dtype == MOE_BF16 ? dh_bf16(p, grid, bn, st) : dh_t<float>(p, grid, bn, st);
+  return dtype == MOE_BF16 ? dh_bf16(p, grid, bn, g.row_tile, st) : dh_t<float>(p, grid, bn, st);
 }
 
 hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du, const void* Wg,
@@ -84,10 +98,10 @@ hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du,
   p.C = dXp; p.ldc = H;
   p.N = H; p.K = 2 * F; p.Kseg = F;
   p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
-  const int bn = pick_bn(H, true);
+  const int bn = g.row_tile == kRowTileLarge ? (H % 256 == 0 ? 256 : 128) : pick_bn(H, true);
   p.ntiles = H / bn;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
-  return dtype == MOE_BF16 ? dx_bf16(p, grid, bn, st) : dx_t<float>(p, grid, bn, st);
+  return dtype == MOE_BF16 ? dx_bf16(p, grid, bn, g.row_tile, st) : dx_t<float>(p, grid, bn, st);
 }
 
 hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, const void* da,

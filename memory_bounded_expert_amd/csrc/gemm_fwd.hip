@@ -7,7 +7,18 @@ namespace moe {
 using namespace gemm;
 
 namespace {
-hipError_t up_swiglu_bf16(const Params& p, dim3 grid, int bn, bool save, hipStream_t st) {
+// 256-row tiles: 4 x 2 waves of 64 x (BN/2) per operand group
+template <int BN>
+using Big = Shape<256, BN, 4, 2, 32, 1>;
+
+hipError_t up_swiglu_bf16(const Params& p, dim3 grid, int bn, bool save, int rt, hipStream_t st) {
+  if (rt == kRowTileLarge) {
+    if (bn == 128)
+      return save ? launch_lds<Mode::Rows, Big<128>, true, true, false, false, Epi::SwiGLUSave>(p, grid, st)
+                  : launch_lds<Mode::Rows, Big<128>, true, true, false, false, Epi::SwiGLU>(p, grid, st);
+    return hipErrorInvalidValue;
+  }
+  if (bn == 256) return launch_lds<Mode::Rows, Shape<128, 256, 2, 4, 32, 1>, true, true, false, false, Epi::SwiGLU>(p, grid, st);
   if (bn == 128) {
     return save ? launch_lds<Mode::Rows, Shape<128, 128, 2, 4, 64, 1>, true, true, false, false, Epi::SwiGLUSave>(p, grid, st)
                 : launch_lds<Mode::Rows, Shape<128, 128, 2, 4, 64, 1>, true, true, false, false, Epi::SwiGLU>(p, grid, st);
@@ -16,7 +27,13 @@ hipError_t up_swiglu_bf16(const Params& p, dim3 grid, int bn, bool save, hipStre
               : launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, true, true, false, false, Epi::SwiGLU>(p, grid, st);
 }
 
-hipError_t down_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
+hipError_t down_bf16(const Params& p, dim3 grid, int bn, int rt, hipStream_t st) {
+  if (rt == kRowTileLarge) {
+    if (bn == 256) return launch_lds<Mode::Rows, Big<256>, false, true, false, false, Epi::Store>(p, grid, st);
+    if (bn == 128) return launch_lds<Mode::Rows, Big<128>, false, true, false, false, Epi::Store>(p, grid, st);
+    return hipErrorInvalidValue;
+  }
+  if (bn == 512) return launch_lds<Mode::Rows, Shape<128, 512, 2, 4, 32, 1>, false, true, false, false, Epi::Store>(p, grid, st);
   if (bn == 256) return launch_lds<Mode::Rows, Shape<128, 256, 2, 4, 64, 1>, false, true, false, false, Epi::Store>(p, grid, st);
   if (bn == 128) return launch_lds<Mode::Rows, Shape<128, 128, 2, 4, 64, 1>, false, true, false, false, Epi::Store>(p, grid, st);
   return launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, false, true, false, false, Epi::Store>(p, grid, st);
@@ -49,11 +66,12 @@ hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const vo
   p.C = h; p.C2 = a; p.C3 = u; p.ldc = F;
   p.N = F; p.K = H;
   p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
-  const int bn = F % 128 == 0 ? 128 : 64;
+  const bool save = a != nullptr;
+  const bool big = g.row_tile == kRowTileLarge;
+  const int bn = (dtype == MOE_BF16 && !save && !big && F % 256 == 0) ? 256 : (F % 128 == 0 ? 128 : 64);
   p.ntiles = F / bn;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
-  const bool save = a != nullptr;
-  return dtype == MOE_BF16 ? up_swiglu_bf16(p, grid, bn, save, st)
+  return dtype == MOE_BF16 ? up_swiglu_bf16(p, grid, bn, save, g.row_tile, st)
                            : up_swiglu_t<float>(p, grid, bn, save, st);
 }
 
@@ -66,10 +84,11 @@ hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd
   p.C = O; p.ldc = H;
   p.N = H; p.K = F;
   p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
-  const int bn = pick_bn(H, true);
+  const int bn = g.row_tile == kRowTileLarge ? (H % 256 == 0 ? 256 : 128)
+                 : (dtype == MOE_BF16 && H % 512 == 0) ? 512 : pick_bn(H, true);
   p.ntiles = H / bn;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
-  return dtype == MOE_BF16 ? down_bf16(p, grid, bn, st) : down_t<float>(p, grid, bn, st);
+  return dtype == MOE_BF16 ? down_bf16(p, grid, bn, g.row_tile, st) : down_t<float>(p, grid, bn, st);
 }
 
 hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bias, float* logits,

@@ -112,7 +112,10 @@ struct LdsCfg {
   static constexpr int B_BYTES = NCOL * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int BUDGET = kLdsBytes / S::WG_PER_CU;
-  static constexpr int NS = (BUDGET / STAGE) > 4 ? 4 : (BUDGET / STAGE);
+  static constexpr int NS_FIT = (BUDGET / STAGE) > 6 ? 6 : (BUDGET / STAGE);
+  // an even stage count keeps the unrolled main loop at NS steps (the two
+  // fragment register sets alternate); odd counts above 3 drop one stage
+  static constexpr int NS = (NS_FIT % 2 == 1 && NS_FIT > 3) ? NS_FIT - 1 : NS_FIT;
   static constexpr int WAVES = S::WGM * S::WGN;
   static constexpr int THREADS = 64 * WAVES;
   // wave-instructions (1 KiB each) per tile, and per wave
@@ -135,7 +138,8 @@ __device__ __forceinline__ int kswz(int r) {
 }
 
 template <Mode MODE, class S, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
-__global__ __launch_bounds__(64 * S::WGM * S::WGN) void gemm_lds_kernel(const Params p) {
+__global__ __launch_bounds__(64 * S::WGM * S::WGN)
+__attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void gemm_lds_kernel(const Params p) {
   using C = LdsCfg<S, DUAL>;
   using T = bf16_t;
   constexpr int BM = S::BM, BN = S::BN, BK = S::BK, NB = C::NB, NS = C::NS, CK = C::CK;
@@ -278,7 +282,10 @@ __global__ __launch_bounds__(64 * S::WGM * S::WGN) void gemm_lds_kernel(const Pa
     }
   };
 
-  const int wm = wave % S::WGM, wn = wave / S::WGM;
+  // waves wave and wave + 4 share a SIMD; with wm = wave / WGN they cover
+  // different row slices, so a tile whose last slices are empty (the ragged
+  // end of an expert segment) leaves each SIMD with less MFMA work
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
   f32x4_t acc[NB][FM][FN];
 #pragma unroll
   for (int g = 0; g < NB; ++g)
@@ -287,77 +294,137 @@ __global__ __launch_bounds__(64 * S::WGM * S::WGN) void gemm_lds_kernel(const Pa
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[g][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // MFMA operand reads
+  // ---- MFMA operand reads.  Every fragment address is a lane-dependent base
+  // plus a compile-time constant (stage, k-step, half, group and fragment
+  // offsets), because each swizzle depends only on the lane:
+  //  * b128 reads of a K-contiguous tile: row r = w0 + f * 16 + l16 and chunk
+  //    c = ks * 4 + lg, with the swizzle a function of l16 alone, so one base
+  //    per k-step and + f * 16 rows per fragment;
+  //  * transposing reads of an M/N-contiguous tile: row k = ks * 32 + lg * 8 +
+  //    trj (+ 4 for the high half), whose swizzle bits (k & 3 and bit 3) come
+  //    from trj and lg alone, so one base per fragment column and + ks * 32 /
+  //    + 4 rows for k-step and half.
+  // The bases are re-laundered every K-step so that the compiler does not
+  // hoist one address register per (stage, fragment) out of the loop.
   const int l16 = lane & 15, lg = lane >> 4;  // column/row within a fragment, k-group
   const int trj = l16 >> 2, trq = l16 & 3;    // transposing read: row j, segment q
-  auto read_tr = [&](const unsigned char* base, int rc_bytes, int k, int col)
-                     __attribute__((always_inline)) -> s16x4_t {
-    // col: first of the 4 columns this lane addresses (a multiple of 4)
-    const int c = col >> 3;
-    const int h = (col >> 2) & 1;
-    const int sw = (rc_bytes >> 4) >= 16 ? trswz<16>(k) : trswz<8>(k);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4_p)(base + k * rc_bytes + ((c ^ sw) << 4) + (h << 3)));
+  constexpr int NBA = A_K ? KS : FM;
+  constexpr int NBB = B_K ? KS : FN;
+  uint32_t baseA[NBA], baseB[NBB];
+  {
+    const uint32_t smem0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_p)smem);
+    auto tr_base = [&](int rc_bytes, int col) -> uint32_t {
+      const int k = lg * 8 + trj;
+      const int sw = (rc_bytes >> 4) >= 16 ? trswz<16>(k) : trswz<8>(k);
+      return (uint32_t)(k * rc_bytes + ((((col >> 3)) ^ sw) << 4) + (((col >> 2) & 1) << 3));
+    };
+#pragma unroll
+    for (int b = 0; b < NBA; ++b) {
+      if constexpr (A_K) {
+        const int r = wm * WM + l16;
+        baseA[b] = smem0 + (uint32_t)(r * (CK * 16) + (((b * 4 + lg) ^ kswz<CK>(r)) << 4));
+      } else {
+        baseA[b] = smem0 + tr_base(RCA * 16, wm * WM + b * 16 + trq * 4);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NBB; ++b) {
+      if constexpr (B_K) {
+        const int n = wn * WN + l16;
+        baseB[b] = smem0 + C::A_BYTES + (uint32_t)(n * (CK * 16) + (((b * 4 + lg) ^ kswz<CK>(n)) << 4));
+      } else {
+        baseB[b] = smem0 + C::A_BYTES + tr_base(RCB * 16, wn * WN + b * 16 + trq * 4);
+      }
+    }
+  }
+  auto launder = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < NBA; ++b) asm volatile("" : "+v"(baseA[b]));
+#pragma unroll
+    for (int b = 0; b < NBB; ++b) asm volatile("" : "+v"(baseB[b]));
+  };
+  auto ld128 = [](uint32_t addr) __attribute__((always_inline)) -> u32x4_t {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((uintptr_t)addr);
+  };
+  auto ldtr = [](uint32_t lo_addr, uint32_t hi_off) __attribute__((always_inline)) -> u32x4_t {
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(uintptr_t)lo_addr);
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(uintptr_t)(lo_addr + hi_off));
+    return __builtin_bit_cast(u32x4_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  auto compute = [&](int s) __attribute__((always_inline)) {
-    const unsigned char* As = stage_a(s);
-    const unsigned char* Bs = stage_b(s);
+  // operand fragments of one K-tile: two register sets, so that the next
+  // tile's fragments are read while the MFMAs consume the current ones
+  u32x4_t fa[2][KS][FM];
+  u32x4_t fb[2][KS][NB][FN];
+  auto read_frags = [&](int s, int set) __attribute__((always_inline)) {
+    const uint32_t so = (uint32_t)(s * C::STAGE);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t af[FM];
-      u32x4_t bv[NB][FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if constexpr (A_K) {
-          const int r = wm * WM + i * 16 + l16;
-          const int c = ks * 4 + lg;
-          af[i] = *reinterpret_cast<const u32x4_t*>(As + r * (CK * 16) + ((c ^ kswz<CK>(r)) << 4));
-        } else {
-          const int kb = ks * 32 + lg * 8 + trj;
-          const int col = wm * WM + i * 16 + trq * 4;
-          const s16x4_t lo = read_tr(As, RCA * 16, kb, col);
-          const s16x4_t hi = read_tr(As, RCA * 16, kb + 4, col);
-          af[i] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
+        if constexpr (A_K)
+          fa[set][ks][i] = ld128(baseA[ks] + so + (uint32_t)(i * 16 * CK * 16));
+        else
+          fa[set][ks][i] = ldtr(baseA[i] + so + (uint32_t)(ks * 32 * RCA * 16), 4 * RCA * 16);
       }
 #pragma unroll
       for (int g = 0; g < NB; ++g)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          if constexpr (B_K) {
-            const int n = wn * WN + j * 16 + l16;
-            const int c = ks * 4 + lg;
-            bv[g][j] = *reinterpret_cast<const u32x4_t*>(Bs + n * (CK * 16) + ((c ^ kswz<CK>(n)) << 4));
-          } else {
-            const unsigned char* Bg = Bs + g * (BK * RCB * 16);
-            const int kb = ks * 32 + lg * 8 + trj;
-            const int col = wn * WN + j * 16 + trq * 4;
-            const s16x4_t lo = read_tr(Bg, RCB * 16, kb, col);
-            const s16x4_t hi = read_tr(Bg, RCB * 16, kb + 4, col);
-            bv[g][j] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
+          if constexpr (B_K)
+            fb[set][ks][g][j] = ld128(baseB[ks] + so + (uint32_t)(j * 16 * CK * 16));
+          else
+            fb[set][ks][g][j] = ldtr(baseB[j] + so + (uint32_t)(g * BK * RCB * 16 + ks * 32 * RCB * 16),
+                                     4 * RCB * 16);
         }
+    }
+  };
+  auto mfmas = [&](int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int g = 0; g < NB; ++g)
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) Mfma<bf16_t>::run(af[i], bv[g][j], acc[g][i][j]);
-    }
+          for (int j = 0; j < FN; ++j) Mfma<bf16_t>::run(fa[set][ks][i], fb[set][ks][g][j], acc[g][i][j]);
   };
 
-  // ---- pipeline: NS stages, NS-1 tiles in flight before the first compute.
-  // Tiles past the last are re-issued as copies of the last one (clamped
-  // index) so that every iteration waits on the same count.
+  // ---- pipeline.  NS stages; tile t goes to stage t % NS.  The prologue
+  // fills every stage and reads tile 0's fragments.  Iteration kt then
+  //   waits until tile kt+1 has landed (this thread's loads, then everyone's,
+  //     via the barrier -- which also orders every wave's reads of tile kt's
+  //     stage before it is refilled),
+  //   refills that stage with tile kt+NS,
+  //   reads tile kt+1's fragments while the MFMAs run on tile kt's.
+  // Tiles past the last are issued as copies of the last one (clamped index)
+  // so that every iteration waits on the same count; the extra fragment read
+  // of the final iteration hits such a copy and is not used.  The loop is
+  // unrolled so that every stage index and register set is a compile-time
+  // constant.
+  constexpr int U = (NS % 2 == 0) ? NS : 2 * NS;
   const int last = nk - 1;
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(min(s, last), s);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt<(NS - 2) * C::PER_TILE>();  // this thread's loads of tile kt landed
-    lds_barrier();                          // everyone's landed; stage kt-1 is free
-    issue(min(kt + NS - 1, last), (kt + NS - 1) % NS);
-    compute(kt % NS);
+  for (int s = 0; s < NS; ++s) issue(min(s, last), s);
+  // a wave whose rows all lie past the segment end only helps with the loads
+  const bool active = m0 + wm * WM < row_end;
+  wait_vmcnt<(NS - 1) * C::PER_TILE>();
+  lds_barrier();
+  if (active) read_frags(0, 0);
+  for (int kt0 = 0; kt0 < nk; kt0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kt = kt0 + u;
+      if (kt >= nk) break;
+      wait_vmcnt<(NS - 2) * C::PER_TILE>();
+      lds_barrier();
+      launder();
+      issue(min(kt + NS, last), u % NS);
+      if (active) {
+        read_frags((u + 1) % NS, (u + 1) & 1);
+        mfmas(u & 1);
+      }
+    }
   }
   wait_vmcnt<0>();
 

@@ -11,8 +11,11 @@
 namespace moe {
 
 // Rows of one M-tile of the row-grouped GEMMs; the planner emits its tile
-// lists in this granularity.
+// lists in this granularity.  bf16 chunks whose experts average at least
+// kRowTileLarge rows use kRowTileLarge (half the weight re-reads per flop);
+// everything else uses kRowTile.
 constexpr int kRowTile = 128;
+constexpr int kRowTileLarge = 256;
 // Tokens per planner block: one wave, one 64-bit membership mask per expert.
 constexpr int kPlanBlock = 64;
 constexpr uint32_t kPlanMagic = 0x4d4f4542u;  // "MOEB"
@@ -34,10 +37,18 @@ inline ChunkGeom chunk_geom(int64_t N, int64_t K, int64_t k, int64_t i) {
 
 inline int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
-// Upper bound on the row-grouped GEMM's M-tiles for a chunk of R pairs:
-// sum_e ceil(M_e / T) <= R / T + (number of non-empty experts).
-inline int64_t max_row_tiles(int64_t R, int E) {
-  return R / kRowTile + (R < E ? R : E);
+// Upper bound on the row-grouped GEMM's M-tiles of T rows for a chunk of R
+// pairs: sum_e ceil(M_e / T) <= R / T + (number of non-empty experts).
+inline int64_t max_row_tiles(int64_t R, int E, int T) {
+  return R / T + (R < E ? R : E);
+}
+// Row tile for a plan: the large tile when the average expert segment of a
+// full chunk (k c_eff rows over E experts) spans at least one large tile.
+inline int row_tile_for(const moe_plan_t& p) {
+  return (p.dtype == MOE_BF16 && p.H % 128 == 0 && p.F % 128 == 0 &&
+          (int64_t)p.k * p.c_eff >= (int64_t)kRowTileLarge * p.E)
+             ? kRowTileLarge
+             : kRowTile;
 }
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
@@ -61,6 +72,7 @@ struct Layout {
   size_t total = 0;
   int64_t nblk = 0;
   int64_t max_tiles = 0;
+  int row_tile = kRowTile;
 };
 
 enum class Pass { Forward, Backward, Debug };
@@ -80,6 +92,7 @@ struct PlanBuffers {
   int32_t* pos;
   int64_t nblk;
   int64_t max_tiles;
+  int row_tile;
 };
 // Plans every chunk at once: counts, scans and scatters the whole batch's
 // routed pairs (O(N k) int32, nothing H-wide).  3 launches.
@@ -111,6 +124,7 @@ struct RowsGeom {
   const int32_t* tile_count;
   const int32_t* offsets;
   int64_t grid_m;  // upper bound on the chunk's M-tiles
+  int row_tile;    // rows per M-tile (kRowTile or kRowTileLarge)
 };
 // h = silu(Xp W_gate[e]) * (Xp W_up[e]) per expert segment; save_au also
 // stores a and u.

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void plan_scan_kernel(int32_t* __restrict
                                                              int32_t* __restrict__ offsets,
                                                              int2* __restrict__ tiles,
                                                              int32_t* __restrict__ tile_count,
-                                                             int64_t max_tiles) {
+                                                             int64_t max_tiles, int row_tile) {
   __shared__ int tot[kMaxE];
   __shared__ int eoff[kMaxE];
   __shared__ int buf[kThreads];
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void plan_scan_kernel(int32_t* __restrict
   int rows = 0, ntile = 0;
   for (int e = e0; e < e1; ++e) {
     rows += tot[e];
-    ntile += (tot[e] + kRowTile - 1) / kRowTile;
+    ntile += (tot[e] + row_tile - 1) / row_tile;
   }
   int row_run = block_inclusive_scan(rows, buf) - rows;
   int tile_run = block_inclusive_scan(ntile, buf) - ntile;
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(kThreads) void plan_scan_kernel(int32_t* __restrict
   for (int e = e0; e < e1; ++e) {
     off[e] = row_run;
     eoff[e] = row_run;
-    const int nt = (tot[e] + kRowTile - 1) / kRowTile;
-    for (int q = 0; q < nt; ++q) tl[tile_run + q] = make_int2(e, row_run + q * kRowTile);
+    const int nt = (tot[e] + row_tile - 1) / row_tile;
+    for (int q = 0; q < nt; ++q) tl[tile_run + q] = make_int2(e, row_run + q * row_tile);
     row_run += tot[e];
     tile_run += nt;
   }
@@ -154,7 +154,7 @@ hipError_t launch_plan(const int32_t* idx, int64_t N, int K, int k, int E, const
                       (size_t)E * sizeof(unsigned long long), st>>>(idx, N, K, k, E, b.nblk,
                                                                     b.blk, b.rank);
   plan_scan_kernel<<<K, kThreads, 0, st>>>(b.blk, E, b.nblk, b.offsets, b.tiles, b.tile_count,
-                                           b.max_tiles);
+                                           b.max_tiles, b.row_tile);
   const int64_t pairs = N * k;
   plan_scatter_kernel<<<(unsigned)ceil_div(pairs, kThreads), kThreads, 0, st>>>(
       idx, N, K, k, E, b.nblk, b.blk, b.rank, b.perm, b.pos);

@@ -52,9 +52,9 @@ def _sample_tokens(N, n=40, seed=0):
     return np.unique(np.concatenate([[0, 1, N - 1], rng.choice(N, n, replace=False)]))
 
 
-def run_workload(name, full=True):
+def run_workload(name, full=True, wl=None, reduced=None):
     require_lib()
-    wl = datagen.WORKLOADS[name]
+    wl = datagen.WORKLOADS[name] if wl is None else wl
     tol = F32_TOL if wl.dtype == "f32" else BF16_TOL
     b = 4 if wl.dtype == "f32" else 2
     say(f"[{name}] generating inputs")
@@ -62,7 +62,7 @@ def run_workload(name, full=True):
     d = DevInputs(inp)
 
     # ---- reduced batch against the full oracle
-    n, c = REDUCED[name]
+    n, c = REDUCED[name] if reduced is None else reduced
     ds = _sub(d, n)
     plan = plan_for(wl, N=n, c=c)
     say(f"[{name}] reduced forward N={n} K={plan.K} c_eff={plan.c_eff}")
@@ -191,3 +191,19 @@ def test_zipf_bf16():
 
 def test_train_bf16():
     run_workload("train_bf16")
+
+
+# Chunks whose experts average 256 rows or more take the 256-row GEMM tiles
+# (bf16, H and F multiples of 128).  This small case lands there: K = 3 chunks
+# of c_eff = 534 tokens, about 267 rows per expert per chunk, so each expert
+# has one full 256-row tile and a ragged one whose upper row slices are empty.
+LARGE_TILE = datagen.WORKLOADS["train_bf16"].with_(
+    name="large_tile_bf16", N=1600, H=256, E=8, k=4, F=384, c=560, K_max=16)
+
+
+def test_large_row_tile_bf16():
+    wl = LARGE_TILE
+    plan = plan_for(wl)
+    assert plan.K == 3 and plan.c_eff == 534
+    assert wl.k * plan.c_eff >= 256 * wl.E and wl.H % 128 == 0 and wl.F % 128 == 0
+    run_workload(wl.name, full=False, wl=wl, reduced=(wl.N, wl.c))
