@@ -35,6 +35,44 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Sources that decide what the forward GEMM kernels do and how they are
+# launched; a traffic record taken with other sources is not used.
+GEMM_SOURCES = ("gemm_lds.hpp", "gemm_kernel.hpp", "gemm_fwd.hip", "device_common.hpp",
+                "moe_internal.h", "plan.hip", "api.hip")
+
+
+def gemm_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "memory_bounded_expert_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE and
+    WRITE_SIZE passes summarised under profiles/ (each scaled by what the same
+    counter reads for a plain device copy of known size), or None when no
+    summary covers the current GEMM sources."""
+    d = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(d):
+        return None
+    sha = gemm_sources_sha256()
+    for name in sorted(os.listdir(d)):
+        if not name.endswith(".md"):
+            continue
+        with open(os.path.join(d, name)) as f:
+            for line in f:
+                if not line.startswith("traffic-record: "):
+                    continue
+                r = json.loads(line[len("traffic-record: "):])
+                if r["workload"] == workload and r["kernel"] == kernel and r["sources_sha256"] == sha:
+                    return int(1024 * (r["fetch_kib_per_dispatch"] * r["fetch_scale"] +
+                                       r["write_kib_per_dispatch"] * r["write_scale"]))
+    return None
+
+
 def stage_work(stage, wl, b, n_i, R_i, E_i):
     """Algorithmic (bytes, flops) of one launch of a stage on a chunk with n_i
     tokens, R_i routed pairs and E_i non-empty experts."""
@@ -208,7 +246,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": d["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(d["GB_per_s"] / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(wl.name, dom)
     roof["kernel"] = dom
     gemm_flops = sum(np.mean([stage_work(s, wl, b, *c)[1] for c in chunks]) * K
                      for s in ("gemm_up", "gemm_down"))

@@ -77,9 +77,14 @@ __device__ __forceinline__ void lds_load16(const i32x4_t& srd, void* lds, uint32
 }
 
 // Work-group barrier for the LDS pipeline: waits for this wave's LDS reads
-// only (outstanding global->LDS loads stay in flight across it).
+// only (outstanding global->LDS loads stay in flight across it).  The wait is
+// the builtin, not inline asm, so that the compiler's own wait-count tracking
+// knows every earlier LDS read has completed and inserts no further waits
+// for those registers.  The immediate is the gfx9 s_waitcnt encoding with
+// vmcnt and expcnt at their maxima (no wait) and lgkmcnt = 0.
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int kWaitLgkm0 = 0xC07F;  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_barrier();
 }
 
