@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the batch the oracle runs for the CPU baseline")
     ap.add_argument("--stage-reps", type=int, default=5)
+    ap.add_argument("--backward", action="store_true",
+                    help="also time forward+backward steps (reported under forward_backward)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -121,7 +123,7 @@ def main():
     bf = wl.dtype == "bf16"
     b = 2 if bf else 4
     log(f"generating {wl.name} inputs")
-    inp = datagen.Inputs(wl, dy=False)
+    inp = datagen.Inputs(wl, dy=args.backward)
 
     def up(a):
         if a is None:
@@ -252,6 +254,55 @@ def main():
                      for s in ("gemm_up", "gemm_down"))
     gemm_us = sum(stages[s]["us_per_launch"] * K for s in ("gemm_up", "gemm_down"))
 
+    fb = None
+    if args.backward:
+        # one step = forward (routing saved) + backward with per-chunk recompute:
+        # dX, dW_gate/up/down (fp32), dlogits, dgates and dW_r
+        dY = up(inp.dY)
+        wsb = B.workspace(plan, "bwd", dev)
+        f32 = torch.float32
+        grads = dict(dX=torch.empty((N, wl.H), dtype=dt, device=dev),
+                 dW_gate=torch.empty((wl.E, wl.H, wl.F), dtype=f32, device=dev),
+                 dW_up=torch.empty((wl.E, wl.H, wl.F), dtype=f32, device=dev),
+                 dW_down=torch.empty((wl.E, wl.F, wl.H), dtype=f32, device=dev),
+                 dlogits=torch.empty((N, wl.E), dtype=f32, device=dev),
+                 dgates=torch.empty((N, k), dtype=f32, device=dev),
+                 dW_r=torch.empty((wl.H, wl.E), dtype=f32, device=dev))
+
+        def bstep():
+            return B.moe_bounded_backward(plan, X, Wr, Wg, Wu, Wd, dY, idx, gates, ws=wsb,
+                                          stream=stream, **grads)
+
+        def fbstep():
+            step()
+            bstep()
+
+        for _ in range(args.warmup):
+            fbstep()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fbstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_fb = e0.elapsed_time(e1) / args.steps
+        e0.record(stream)
+        for _ in range(args.steps):
+            bstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_b = e0.elapsed_time(e1) / args.steps
+        # backward GEMM flops: 12 H F per pair, plus the 4 H F per pair recompute
+        bflops = 16.0 * pairs * wl.H * wl.F
+        fb = {"ms_per_step": round(ms_fb, 4), "pairs_per_s": round(pairs / (ms_fb / 1e3), 1),
+              "backward_ms": round(ms_b, 4),
+              "backward_gemm_TFLOP_per_s": round(bflops / (ms_b / 1e3) / 1e12, 1),
+              "workspace_bytes": plan.bwd_workspace_bytes}
+        log(f"forward+backward: {ms_fb:.3f} ms/step, {fb['pairs_per_s']:.4g} pairs/s; "
+            f"backward {ms_b:.3f} ms ({fb['backward_gemm_TFLOP_per_s']} TFLOP/s over its GEMM flops)")
+
     p1 = B.moe_plan_chunks(wl.N, wl.H, wl.F, wl.E, wl.k, wl.c, 1, plan.dtype)
     out = {
         "metric": "routed token-expert pairs/s (forward) at bounded dispatch buffer",
@@ -269,6 +320,7 @@ def main():
         "config": {"workload": wl.name, "N": N, "H": wl.H, "E": wl.E, "top_k": k, "F": wl.F,
                    "c": wl.c, "K_max": wl.K_max, "K": K, "c_eff": plan.c_eff,
                    "parallelism": "single GPU"},
+        "forward_backward": fb,
         "roofline": roof,
         "grouped_gemm": {"TFLOP_per_s": round(gemm_flops / gemm_us / 1e6, 1),
                          "mfma_frac": round(gemm_flops / gemm_us / 1e6 / peak_tf, 4)},

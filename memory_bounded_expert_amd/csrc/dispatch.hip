@@ -212,8 +212,6 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
   }
 }
 
-// dW_r[:, e] += sum over chunk rows r of expert e of dlogits[t(r), e] Xp[r, :].
-// Grid (column blocks, E); each thread owns one 16-byte column chunk.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dwr_kernel(const T* __restrict__ Xp,
                                                        const int32_t* __restrict__ perm,
@@ -221,26 +219,56 @@ __global__ __launch_bounds__(kThreads) void dwr_kernel(const T* __restrict__ Xp,
                                                        const float* __restrict__ dlogits,
                                                        float* __restrict__ dWr, int k, int E,
                                                        int H, int64_t N) {
+  // dW_r[:, e] += sum over the chunk's rows r of expert e of
+  // Xp[r, :] * dlogits[t(r), e]; rows of other experts would add
+  // dlogits[t, e] = 0 exactly, so they are skipped.  One work-group per
+  // (64-wide column block of H, expert): CPB threads cover a row's 64 values
+  // with 16-byte loads and RG row groups stride the expert's segment (rows
+  // ascending per thread); the groups' partial sums are then added in group
+  // order, so the result does not depend on timing.
   constexpr int EPC = Elem<T>::kPer16B;
+  constexpr int COLS = 64;
+  constexpr int CPB = COLS / EPC;
+  constexpr int RG = kThreads / CPB;
+  __shared__ float part[RG][COLS + 1];
   const int e = blockIdx.y;
-  const int c = blockIdx.x * kThreads + threadIdx.x;
-  if (c * EPC >= H) return;
+  const int cb = blockIdx.x;
+  const int cg = threadIdx.x % CPB, rg = threadIdx.x / CPB;
   const int r0 = offsets[e], r1 = offsets[e + 1];
   if (r1 <= r0) return;
+  const int64_t col = (int64_t)cb * COLS + cg * EPC;
   float acc[EPC];
 #pragma unroll
   for (int q = 0; q < EPC; ++q) acc[q] = 0.f;
-  for (int r = r0; r < r1; ++r) {
+  auto row = [&](int r, float& d, float* v) __attribute__((always_inline)) {
     const int64_t t = perm[r] / k;
-    if ((uint64_t)t >= (uint64_t)N) continue;  // only on a corrupt plan
-    const float d = dlogits[t * E + e];
-    float v[EPC];
-    unpack16(reinterpret_cast<const u32x4_t*>(Xp + (int64_t)r * H)[c], v, T());
+    d = (uint64_t)t < (uint64_t)N ? dlogits[t * E + e] : 0.f;  // t >= N only on a corrupt plan
+    unpack16(*reinterpret_cast<const u32x4_t*>(Xp + (int64_t)r * H + col), v, T());
+  };
+  int r = r0 + rg;
+  for (; r + 3 * RG < r1; r += 4 * RG) {
+    float d[4], v[4][EPC];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) row(r + j * RG, d[j], v[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < EPC; ++q) acc[q] = fmaf(d[j], v[j][q], acc[q]);
+  }
+  for (; r < r1; r += RG) {
+    float d, v[EPC];
+    row(r, d, v);
 #pragma unroll
     for (int q = 0; q < EPC; ++q) acc[q] = fmaf(d, v[q], acc[q]);
   }
 #pragma unroll
-  for (int q = 0; q < EPC; ++q) dWr[(int64_t)(c * EPC + q) * E + e] += acc[q];
+  for (int q = 0; q < EPC; ++q) part[rg][cg * EPC + q] = acc[q];
+  __syncthreads();
+  if (threadIdx.x < COLS) {
+    float s = 0.f;
+    for (int g = 0; g < RG; ++g) s += part[g][threadIdx.x];
+    dWr[((int64_t)cb * COLS + threadIdx.x) * E + e] += s;
+  }
 }
 
 }  // namespace
@@ -332,8 +360,8 @@ hipError_t launch_combine_bwd(int dtype, const void* dXp, const void* WrT, const
 hipError_t launch_dwr(int dtype, const void* Xp, const int32_t* perm, const int32_t* offsets,
                       const float* dlogits, float* dWr, int k, int E, int H, int64_t N,
                       hipStream_t st) {
-  const int EPC = dtype == MOE_BF16 ? 8 : 4;
-  const dim3 grid((unsigned)ceil_div(H / EPC, kThreads), (unsigned)E);
+  // H is a multiple of 64 (checked when the plan is made)
+  const dim3 grid((unsigned)(H / 64), (unsigned)E);
   if (dtype == MOE_BF16)
     dwr_kernel<bf16_t><<<grid, kThreads, 0, st>>>((const bf16_t*)Xp, perm, offsets, dlogits, dWr, k,
                                                   E, H, N);

@@ -433,6 +433,50 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
   }
   wait_vmcnt<0>();
 
+  if constexpr (EPI == Epi::AccF32) {
+    // Weight-gradient accumulation C += tile (fp32 read-modify-write), staged
+    // through LDS so that HBM sees 16-byte, row-contiguous loads and stores
+    // instead of the fragments' 4-byte scatter.  Each element is still
+    // old + new in one fp32 add.  The operand stages are free: every load has
+    // landed (vmcnt 0 above) and the barrier orders every wave's last fragment
+    // reads before the overwrite.  Rows are padded by 4 floats so the four row
+    // groups of a fragment land in distinct banks.
+    constexpr int LD = BN + 4;
+    constexpr int V = BN / 4;  // 16-byte vectors per tile row
+    constexpr int PER = BM * V / C::THREADS;
+    static_assert(NB * BM * LD * 4 <= NS * C::STAGE, "accumulator staging must fit the LDS stages");
+    static_assert((BM * V) % C::THREADS == 0, "tile rows must split over the threads");
+    float* stg = reinterpret_cast<float*>(smem);
+    lds_barrier();
+#pragma unroll
+    for (int g = 0; g < NB; ++g)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            stg[g * BM * LD + (wm * WM + i * 16 + 4 * lg + q) * LD + wn * WN + j * 16 + l16] = acc[g][i][j][q];
+    lds_barrier();
+#pragma unroll
+    for (int g = 0; g < NB; ++g) {
+      float* Cg = static_cast<float*>(g == 0 ? p.C : p.C2) + (int64_t)e * p.c_estride;
+      f32x4_t old[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int idx = tid + u * C::THREADS, r = idx / V, c4 = idx - r * V;
+        old[u] = *reinterpret_cast<const f32x4_t*>(Cg + (int64_t)(m0 + r) * p.ldc + n0 + c4 * 4);
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int idx = tid + u * C::THREADS, r = idx / V, c4 = idx - r * V;
+        const f32x4_t add = *reinterpret_cast<const f32x4_t*>(stg + g * BM * LD + r * LD + c4 * 4);
+        *reinterpret_cast<f32x4_t*>(Cg + (int64_t)(m0 + r) * p.ldc + n0 + c4 * 4) = old[u] + add;
+      }
+    }
+    return;
+  }
+
   // ---- epilogue (as gemm_kernel.hpp)
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -459,13 +503,6 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
           static_cast<float*>(p.C)[o] = v0;
         } else if constexpr (EPI == Epi::BiasF32) {
           if (gcol < p.N) static_cast<float*>(p.C)[o] = v0 + (p.bias ? p.bias[gcol] : 0.f);
-        } else {  // AccF32
-          float* Cp = static_cast<float*>(p.C) + (int64_t)e * p.c_estride;
-          Cp[o] += v0;
-          if constexpr (DUAL) {
-            float* C2p = static_cast<float*>(p.C2) + (int64_t)e * p.c_estride;
-            C2p[o] += acc[1][i][j][q];
-          }
         }
       }
 }
