@@ -35,13 +35,13 @@ hipError_t dx_bf16(const Params& p, dim3 grid, int bn, int rt, hipStream_t st) {
 
 template <int BM>
 hipError_t wgu_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
-  if (bn == 128) return launch_lds<Mode::Expert, Shape<BM, 128, 2, 4, 64, 1>, true, false, false, false, Epi::AccF32>(p, grid, st);
+  if (bn == 128) return launch_lds<Mode::Expert, Shape<BM, 128, 2, 2, 32, 2>, true, false, false, false, Epi::AccF32>(p, grid, st);
   return launch_lds<Mode::Expert, Shape<BM, 64, 2, 4, 64, 1>, true, false, false, false, Epi::AccF32>(p, grid, st);
 }
 
 template <int BM>
 hipError_t wd_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
-  if (bn == 256) return launch_lds<Mode::Expert, Shape<BM, 256, 2, 4, 64, 1>, false, false, false, false, Epi::AccF32>(p, grid, st);
+  if (bn == 256) return launch_lds<Mode::Expert, Shape<BM, 256, 2, 2, 32, 2>, false, false, false, false, Epi::AccF32>(p, grid, st);
   if (bn == 128) return launch_lds<Mode::Expert, Shape<BM, 128, 2, 4, 64, 1>, false, false, false, false, Epi::AccF32>(p, grid, st);
   return launch_lds<Mode::Expert, Shape<BM, 64, 2, 4, 64, 1>, false, false, false, false, Epi::AccF32>(p, grid, st);
 }

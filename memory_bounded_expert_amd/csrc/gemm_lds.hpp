@@ -439,39 +439,48 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
     // instead of the fragments' 4-byte scatter.  Each element is still
     // old + new in one fp32 add.  The operand stages are free: every load has
     // landed (vmcnt 0 above) and the barrier orders every wave's last fragment
-    // reads before the overwrite.  Rows are padded by 4 floats so the four row
-    // groups of a fragment land in distinct banks.
+    // reads before the overwrite.  The tile goes through in slabs of SLAB wave
+    // row slices (as many as the stages hold); rows are padded by 4 floats so
+    // the four row groups of a fragment land in distinct banks.
     constexpr int LD = BN + 4;
     constexpr int V = BN / 4;  // 16-byte vectors per tile row
-    constexpr int PER = BM * V / C::THREADS;
-    static_assert(NB * BM * LD * 4 <= NS * C::STAGE, "accumulator staging must fit the LDS stages");
-    static_assert((BM * V) % C::THREADS == 0, "tile rows must split over the threads");
+    constexpr int SLAB_FIT = (NS * C::STAGE) / (WM * LD * 4);
+    constexpr int SLAB = SLAB_FIT >= S::WGM ? S::WGM : (SLAB_FIT >= 2 && S::WGM % 2 == 0 ? 2 : 1);
+    constexpr int SR = SLAB * WM;  // rows per slab
+    constexpr int PER = SR * V / C::THREADS;
+    static_assert(SR * LD * 4 <= NS * C::STAGE, "accumulator staging must fit the LDS stages");
+    static_assert(S::WGM % SLAB == 0 && (SR * V) % C::THREADS == 0, "slab must split over the threads");
     float* stg = reinterpret_cast<float*>(smem);
-    lds_barrier();
-#pragma unroll
-    for (int g = 0; g < NB; ++g)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            stg[g * BM * LD + (wm * WM + i * 16 + 4 * lg + q) * LD + wn * WN + j * 16 + l16] = acc[g][i][j][q];
-    lds_barrier();
 #pragma unroll
     for (int g = 0; g < NB; ++g) {
       float* Cg = static_cast<float*>(g == 0 ? p.C : p.C2) + (int64_t)e * p.c_estride;
-      f32x4_t old[PER];
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int idx = tid + u * C::THREADS, r = idx / V, c4 = idx - r * V;
-        old[u] = *reinterpret_cast<const f32x4_t*>(Cg + (int64_t)(m0 + r) * p.ldc + n0 + c4 * 4);
-      }
+      for (int sl = 0; sl < S::WGM / SLAB; ++sl) {
+        lds_barrier();  // previous users of the LDS are done
+        if (wm / SLAB == sl) {
+          const int r0 = (wm - sl * SLAB) * WM;
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int idx = tid + u * C::THREADS, r = idx / V, c4 = idx - r * V;
-        const f32x4_t add = *reinterpret_cast<const f32x4_t*>(stg + g * BM * LD + r * LD + c4 * 4);
-        *reinterpret_cast<f32x4_t*>(Cg + (int64_t)(m0 + r) * p.ldc + n0 + c4 * 4) = old[u] + add;
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                stg[(r0 + i * 16 + 4 * lg + q) * LD + wn * WN + j * 16 + l16] = acc[g][i][j][q];
+        }
+        lds_barrier();
+        const int row0 = m0 + sl * SR;
+        f32x4_t old[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const int idx = tid + u * C::THREADS, r = idx / V, c4 = idx - r * V;
+          old[u] = *reinterpret_cast<const f32x4_t*>(Cg + (int64_t)(row0 + r) * p.ldc + n0 + c4 * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const int idx = tid + u * C::THREADS, r = idx / V, c4 = idx - r * V;
+          const f32x4_t add = *reinterpret_cast<const f32x4_t*>(stg + r * LD + c4 * 4);
+          *reinterpret_cast<f32x4_t*>(Cg + (int64_t)(row0 + r) * p.ldc + n0 + c4 * 4) = old[u] + add;
+        }
       }
     }
     return;
