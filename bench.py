@@ -2,7 +2,8 @@
 """Benchmark of the memory-bounded MoE layer forward pass on one MI355X.
 
 One step = one full forward pass of the layer (router GEMM, top-k and gates,
-chunk plan, and per chunk: gather, gate/up grouped GEMM with SwiGLU, down
+chunk plan, and per chunk: gather (in bf16 folded into the next GEMM's
+operand loads), gate/up grouped GEMM with SwiGLU, down
 grouped GEMM, gate-weighted combine) over one batch of synthetic inputs that
 are resident in HBM before the timed region starts.
 
@@ -203,7 +204,15 @@ def main():
                          "launches_per_step": 1}
     # per-chunk stages: replay the chunk loop in order (so every launch sees
     # the same buffers as in the forward call), one event pair per launch
-    per_chunk = ("gather", "gemm_up", "gemm_down", "combine")
+    per_chunk = ["gather", "gemm_up", "gemm_down", "combine"]
+    try:  # the bf16 forward reads its permuted inputs inside the gate/up GEMM
+        B.moe_debug_stage(plan, "gather", 0, X, Wr, bias, Wg, Wu, Wd, Y, idx, gates, ws,
+                          stream=stream)
+    except B.MoeError as err_:
+        if err_.status != B.MOE_EUNSUPPORTED:
+            raise
+        per_chunk.remove("gather")
+        log("  (no gather kernel: the gate/up GEMM reads the permuted rows from X)")
     marks = {s_: [] for s_ in per_chunk}
     for _ in range(args.stage_reps):
         for i in range(K):

@@ -29,8 +29,10 @@
  * Each chunk's routed pairs are permuted into an expert-contiguous buffer of
  * at most k*c_eff rows, run through the experts and combined back, so the
  * top-k-expanded buffer of the whole batch never exists.  The H-wide
- * dispatch buffers take 2*k*c_eff*H*b bytes ([BSO] "Memory bound" with
- * E_p = 1 and c read as c_eff).  The result does not depend on K: per-token
+ * dispatch buffers take at most 2*k*c_eff*H*b bytes ([BSO] "Memory bound"
+ * with E_p = 1 and c read as c_eff); the bf16 forward needs only half of
+ * that, because its gate/up GEMM reads each permuted input row straight from
+ * X.  The result does not depend on K: per-token
  * outputs are bitwise identical for every (c, K_max).
  *
  * Conventions for every entry point:
@@ -93,7 +95,10 @@ typedef struct moe_stats {
     int32_t launches;            /* kernels enqueued                          */
     int64_t c_eff;
     int64_t max_pairs_per_chunk; /* largest R_i = k * n_i over the chunks     */
-    int64_t dispatch_bytes;      /* H-wide per-chunk dispatch buffers carved  */
+    int64_t dispatch_bytes;      /* H-wide per-chunk dispatch buffers carved:
+                                    k*c_eff*H*b each; one in the bf16 forward
+                                    (expert outputs; inputs read from X in
+                                    place), two otherwise                     */
     int64_t dispatch_bound_bytes;/* 2 * k * c_eff * H * b                     */
     int64_t intermediate_bytes;  /* F-wide per-chunk intermediates            */
     int64_t workspace_bytes;     /* workspace bytes the call used             */
@@ -127,8 +132,10 @@ int moe_plan_chunks(int64_t N, int32_t H, int32_t F, int32_t E, int32_t k,
  *   moe_bounded_backward needs.
  * workspace: device memory of at least plan->fwd_workspace_bytes bytes,
  *   256-byte aligned; its contents on entry do not matter.  It holds the
- *   whole batch's O(N*k) int32 routing plan and the per-chunk buffers
- *   (two H-wide dispatch buffers of k*c_eff rows and one F-wide one).
+ *   whole batch's O(N*k) int32 routing plan and the per-chunk buffers: the
+ *   F-wide SwiGLU output and the H-wide expert outputs, k*c_eff rows each,
+ *   plus (fp32, or bf16 with N*H*2 >= 2^31) an H-wide permuted-input buffer;
+ *   otherwise the gate/up GEMM reads the permuted rows straight from X.
  * stats: optional host struct, filled on success.
  * Errors: MOE_EINVAL (plan not from moe_plan_chunks, a required pointer is
  *   NULL, workspace not 256-byte aligned), MOE_EWORKSPACE (workspace_bytes <
@@ -215,12 +222,16 @@ int moe_debug_plan(const moe_plan_t* plan, const int32_t* topk_idx,
  * (0 <= chunk < plan->K), reading and writing the same buffers.  Running
  * GATHER, GEMM_UP, GEMM_DOWN and COMBINE for chunks 0..K-1 in that order
  * reproduces the forward call's outputs bitwise; a stage run out of that
- * order computes on whatever the per-chunk buffers hold.
+ * order computes on whatever the per-chunk buffers hold.  When the plan's
+ * forward reads the permuted inputs in place (see moe_bounded_forward's
+ * workspace), it has no gather kernel: GATHER then returns MOE_EUNSUPPORTED
+ * and enqueues nothing.
  * stage: MOE_STAGE_ROUTER (router logits, whole batch), MOE_STAGE_TOPK (top-k
  *   and gates, whole batch), MOE_STAGE_PLAN (planner, whole batch),
  *   MOE_STAGE_GATHER, MOE_STAGE_GEMM_UP (gate/up GEMM + SwiGLU),
  *   MOE_STAGE_GEMM_DOWN, MOE_STAGE_COMBINE (per chunk).
  * Errors: MOE_EINVAL for a bad plan, stage, chunk or NULL pointer;
+ *   MOE_EUNSUPPORTED for GATHER when the forward has no gather kernel;
  *   MOE_EWORKSPACE as moe_bounded_forward.
  */
 enum moe_stage {

@@ -46,7 +46,8 @@ Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_d
     L.perm = take(N * k * 4);
     L.pos = take(N * k * 4);
     const size_t rows = k * ce;
-    L.xp = take(rows * H * b);
+    // the bf16 forward reads its permuted inputs straight from X
+    if (pass == Pass::Backward || !fused_gather(p)) L.xp = take(rows * H * b);
     L.o = take(rows * H * b);
     L.h = take(rows * F * b);
     if (pass == Pass::Backward) {
@@ -91,14 +92,15 @@ RowsGeom rows_geom(const PlanBuffers& b, const moe_plan_t& P, int i, int64_t R) 
   return g;
 }
 
-void fill_stats(moe_stats_t* s, const moe_plan_t& P, int launches, size_t ws, size_t inter) {
+void fill_stats(moe_stats_t* s, const moe_plan_t& P, int launches, size_t ws, size_t inter,
+                int hbufs = 2) {
   if (!s) return;
   std::memset(s, 0, sizeof(*s));
   s->K = P.K;
   s->launches = launches;
   s->c_eff = P.c_eff;
   s->max_pairs_per_chunk = (int64_t)P.k * P.c_eff;  // chunk 0 holds c_eff tokens
-  s->dispatch_bytes = 2 * (int64_t)P.k * P.c_eff * P.H * elem_bytes(P.dtype);
+  s->dispatch_bytes = hbufs * (int64_t)P.k * P.c_eff * P.H * elem_bytes(P.dtype);
   s->dispatch_bound_bytes = P.dispatch_bound_bytes;
   s->intermediate_bytes = (int64_t)inter;
   s->workspace_bytes = (int64_t)ws;
@@ -187,6 +189,7 @@ MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const voi
   const PlanBuffers pb = plan_buffers(ws, L, nullptr, nullptr, nullptr);
   MOE_CHECK(launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st));
   launches += 2;
+  const bool fused = fused_gather(P);
   void* xp = ws + L.xp;
   void* o = ws + L.o;
   void* h = ws + L.h;
@@ -195,13 +198,18 @@ MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const voi
     const int64_t R = (int64_t)P.k * g.n;
     const RowsGeom rg = rows_geom(pb, P, i, R);
     const int32_t* perm_i = pb.perm + g.pair_base;
-    MOE_CHECK(launch_gather(P.dtype, X, xp, perm_i, R, P.k, P.N, P.H, st));
-    MOE_CHECK(gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st));
+    if (fused) {
+      MOE_CHECK(gemm_up_swiglu(P.dtype, rg, X, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st,
+                               perm_i, P.k, P.N));
+    } else {
+      MOE_CHECK(launch_gather(P.dtype, X, xp, perm_i, R, P.k, P.N, P.H, st));
+      MOE_CHECK(gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st));
+    }
     MOE_CHECK(gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st));
     MOE_CHECK(launch_combine(P.dtype, o, pb.pos, gates, Y, P.N, P.K, i, g.n, P.k, P.H, st));
   }
   fill_stats(stats, P, launches, L.total,
-             (size_t)P.k * P.c_eff * P.F * elem_bytes(P.dtype));
+             (size_t)P.k * P.c_eff * P.F * elem_bytes(P.dtype), fused ? 1 : 2);
   return MOE_OK;
 }
 
@@ -311,6 +319,8 @@ MOE_API int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk
     return MOE_EINVAL;
   if ((uintptr_t)workspace % 256) return MOE_EINVAL;
   if (workspace_bytes < (size_t)P.fwd_workspace_bytes) return MOE_EWORKSPACE;
+  const bool fused = fused_gather(P);
+  if (stage == MOE_STAGE_GATHER && fused) return MOE_EUNSUPPORTED;  // no gather kernel
   const Layout L = make_layout(P, Pass::Forward, true, false);
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -328,15 +338,19 @@ MOE_API int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk
     const ChunkGeom g = chunk_geom(P.N, P.K, P.k, chunk);
     const int64_t R = (int64_t)P.k * g.n;
     const RowsGeom rg = rows_geom(pb, P, chunk, R);
+    const int32_t* perm_i = pb.perm + g.pair_base;
     void* xp = ws + L.xp;
     void* o = ws + L.o;
     void* h = ws + L.h;
     switch (stage) {
       case MOE_STAGE_GATHER:
-        err = launch_gather(P.dtype, X, xp, pb.perm + g.pair_base, R, P.k, P.N, P.H, st);
+        err = launch_gather(P.dtype, X, xp, perm_i, R, P.k, P.N, P.H, st);
         break;
       case MOE_STAGE_GEMM_UP:
-        err = gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st);
+        err = fused ? gemm_up_swiglu(P.dtype, rg, X, W_gate, W_up, h, nullptr, nullptr, P.H, P.F,
+                                     st, perm_i, P.k, P.N)
+                    : gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, nullptr, nullptr, P.H,
+                                     P.F, st);
         break;
       case MOE_STAGE_GEMM_DOWN:
         err = gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st);

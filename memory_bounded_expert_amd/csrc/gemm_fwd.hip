@@ -58,10 +58,15 @@ hipError_t down_t(const Params& p, dim3 grid, int bn, hipStream_t st) {
 }  // namespace
 
 hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const void* Wg,
-                          const void* Wu, void* h, void* a, void* u, int H, int F, hipStream_t st) {
+                          const void* Wu, void* h, void* a, void* u, int H, int F, hipStream_t st,
+                          const int32_t* rows, int k, int64_t x_rows) {
   if (g.grid_m == 0) return hipSuccess;
   Params p{};
   p.A = Xp; p.lda = H;
+  if (rows) {
+    if (dtype != MOE_BF16) return hipErrorInvalidValue;
+    p.a_rows = rows; p.a_row_div = k; p.a_src_rows = x_rows;
+  }
   p.B = Wg; p.B2 = Wu; p.ldb = F; p.b_estride = (int64_t)H * F;
   p.C = h; p.C2 = a; p.C3 = u; p.ldc = F;
   p.N = F; p.K = H;

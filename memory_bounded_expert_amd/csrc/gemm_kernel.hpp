@@ -62,6 +62,12 @@ struct Params {
   const int32_t* tile_count;
   const int32_t* offsets;
   const float* bias;
+  // Rows mode, LDS pipeline only: when set, row r of A is row
+  // a_rows[r] / a_row_div of the matrix at A (a_src_rows rows): the permuted
+  // input is read straight from X through the chunk's permutation.
+  const int32_t* a_rows;
+  int a_row_div;
+  int64_t a_src_rows;
 };
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }

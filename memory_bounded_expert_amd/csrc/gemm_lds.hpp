@@ -211,9 +211,32 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
 
   // ---- per-tile buffer resources (offsets below are tile-relative)
   i32x4_t rA, rA2, rB, rB2;
+  // Row-indexed A (Rows mode): byte offset of the source row of each of this
+  // lane's A-load rows, or kOob past the segment end.
+  constexpr int RPIK = 64 / CK;  // K-contiguous rows per load instruction
+  uint32_t arow[C::A_PW];
+  const bool gathered = MODE == Mode::Rows && A_K && !KCAT && p.a_rows != nullptr;
   if constexpr (A_K) {
     const int64_t rows = (int64_t)min(row_end - m0, BM);
-    rA = make_srd(Ap + (int64_t)m0 * p.lda, rows * p.lda * TS);
+    if (gathered) {
+      rA = make_srd(Ap, p.a_src_rows * p.lda * TS);
+#pragma unroll
+      for (int u = 0; u < C::A_PW; ++u) {
+        const int row = (wave * C::A_PW + u) * RPIK + lane / CK;
+        arow[u] = kOob;
+        if (row < rows) {
+          const int src = p.a_rows[m0 + row] / p.a_row_div;
+          if ((uint64_t)src < (uint64_t)p.a_src_rows) arow[u] = (uint32_t)((int64_t)src * p.lda * TS);
+        }
+      }
+    } else {
+      rA = make_srd(Ap + (int64_t)m0 * p.lda, rows * p.lda * TS);
+#pragma unroll
+      for (int u = 0; u < C::A_PW; ++u) {
+        const int row = (wave * C::A_PW + u) * RPIK + lane / CK;
+        arow[u] = (uint32_t)(row * p.lda * TS);
+      }
+    }
     rA2 = KCAT ? make_srd(A2p + (int64_t)m0 * p.lda, rows * p.lda * TS) : rA;
   } else {
     rA = make_srd(Ap + k_begin * p.lda + m0, (int64_t)k_len * p.lda * TS);
@@ -241,7 +264,6 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
       second = k0 >= p.Kseg;
       kk = second ? k0 - p.Kseg : k0;
     }
-    constexpr int RPIK = 64 / CK;  // K-contiguous rows per instruction
     // A
 #pragma unroll
     for (int u = 0; u < C::A_PW; ++u) {
@@ -250,7 +272,8 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
       if constexpr (A_K) {
         const int row = ins * RPIK + lane / CK;
         const int c = (lane % CK) ^ kswz<CK>(row);
-        lds_load16(second ? rA2 : rA, dst, (uint32_t)((row * p.lda + kk + c * 8) * TS));
+        const uint32_t off = arow[u] == kOob ? kOob : arow[u] + (uint32_t)((kk + c * 8) * TS);
+        lds_load16(second ? rA2 : rA, dst, off);
       } else {
         constexpr int RPI = 64 / RCA;
         const int k = ins * RPI + lane / RCA;

@@ -37,6 +37,13 @@ inline ChunkGeom chunk_geom(int64_t N, int64_t K, int64_t k, int64_t i) {
 
 inline int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
+// The bf16 forward reads each chunk's permuted input rows straight from X
+// inside the gate/up GEMM (no gather kernel, no permuted-input buffer) when X
+// fits one buffer resource's 32-bit offsets.
+inline bool fused_gather(const moe_plan_t& p) {
+  return p.dtype == MOE_BF16 && (int64_t)p.N * p.H * 2 <= 0x7FFFFFF0LL;
+}
+
 // Upper bound on the row-grouped GEMM's M-tiles of T rows for a chunk of R
 // pairs: sum_e ceil(M_e / T) <= R / T + (number of non-empty experts).
 inline int64_t max_row_tiles(int64_t R, int E, int T) {
@@ -127,9 +134,11 @@ struct RowsGeom {
   int row_tile;    // rows per M-tile (kRowTile or kRowTileLarge)
 };
 // h = silu(Xp W_gate[e]) * (Xp W_up[e]) per expert segment; save_au also
-// stores a and u.
+// stores a and u.  With rows != nullptr (bf16 only), Xp is not a buffer:
+// row r is row rows[r] / k of X (x_rows rows), read straight from X.
 hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const void* Wg,
-                          const void* Wu, void* h, void* a, void* u, int H, int F, hipStream_t st);
+                          const void* Wu, void* h, void* a, void* u, int H, int F, hipStream_t st,
+                          const int32_t* rows = nullptr, int k = 1, int64_t x_rows = 0);
 // O = h W_down[e]
 hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd, void* O, int H,
                      int F, hipStream_t st);
