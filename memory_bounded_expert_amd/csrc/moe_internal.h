@@ -11,11 +11,16 @@
 namespace moe {
 
 // Rows of one M-tile of the row-grouped GEMMs; the planner emits its tile
-// lists in this granularity.  bf16 chunks whose experts average at least
-// kRowTileLarge rows use kRowTileLarge (half the weight re-reads per flop);
-// everything else uses kRowTile.
+// lists in this granularity.  Each M-tile streams its expert's whole weight
+// slice, so an expert segment just over one tile costs two weight passes.
+// bf16 chunks whose experts average at least kLargeTileMinRows rows use
+// kRowTileLarge: under balanced routing segments cluster around the mean, and
+// at a mean of about 128 rows half of them would spill into a second, almost
+// empty 128-row tile.  (Under skewed routing the mean says little; the plan
+// has no routing data to tell.)  Everything else uses kRowTile.
 constexpr int kRowTile = 128;
 constexpr int kRowTileLarge = 256;
+constexpr int kLargeTileMinRows = 96;
 // Tokens per planner block: one wave, one 64-bit membership mask per expert.
 constexpr int kPlanBlock = 64;
 constexpr uint32_t kPlanMagic = 0x4d4f4542u;  // "MOEB"
@@ -50,10 +55,10 @@ inline int64_t max_row_tiles(int64_t R, int E, int T) {
   return R / T + (R < E ? R : E);
 }
 // Row tile for a plan: the large tile when the average expert segment of a
-// full chunk (k c_eff rows over E experts) spans at least one large tile.
+// full chunk (k c_eff rows over E experts) has at least kLargeTileMinRows rows.
 inline int row_tile_for(const moe_plan_t& p) {
   return (p.dtype == MOE_BF16 && p.H % 128 == 0 && p.F % 128 == 0 &&
-          (int64_t)p.k * p.c_eff >= (int64_t)kRowTileLarge * p.E)
+          (int64_t)p.k * p.c_eff >= (int64_t)kLargeTileMinRows * p.E)
              ? kRowTileLarge
              : kRowTile;
 }
