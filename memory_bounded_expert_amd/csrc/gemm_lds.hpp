@@ -451,6 +451,20 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
       if (active) {
         read_frags((u + 1) % NS, (u + 1) & 1);
         mfmas(u & 1);
+        // Issue order: one MFMA, then one fragment read, pair by pair, then
+        // whatever is left.  Spreading the LDS reads evenly over the MFMA
+        // phase keeps the LDS command queue from filling (a full queue
+        // stalls the wave's in-order issue, MFMAs included).
+        constexpr int NRD = KS * (A_K ? FM : 2 * FM) + KS * NB * FN * (B_K ? 1 : 2);
+        constexpr int NMF = KS * NB * FM * FN;
+        constexpr int PAIRS = NRD < NMF ? NRD : NMF;
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        if constexpr (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
+        if constexpr (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
       }
     }
   }
