@@ -231,9 +231,14 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
   int launches = 0;
   (void)hipGetLastError();
   const size_t wbytes = (size_t)P.E * P.H * P.F * sizeof(float);
-  MOE_CHECK(launch_fill_zero(dW_gate, wbytes, st));
-  MOE_CHECK(launch_fill_zero(dW_up, wbytes, st));
-  MOE_CHECK(launch_fill_zero(dW_down, wbytes, st));
+  // bf16: chunk 0's weight-gradient products store dW (zeros for experts
+  // without rows) and later chunks accumulate; fp32 accumulates from zero
+  const bool wg_init = P.dtype == MOE_BF16 && P.N > 0;
+  if (!wg_init) {
+    MOE_CHECK(launch_fill_zero(dW_gate, wbytes, st));
+    MOE_CHECK(launch_fill_zero(dW_up, wbytes, st));
+    MOE_CHECK(launch_fill_zero(dW_down, wbytes, st));
+  }
   if (dW_r) MOE_CHECK(launch_fill_zero(dW_r, (size_t)P.H * P.E * sizeof(float), st));
   if (P.N == 0) {
     fill_stats(stats, P, launches, 0, 0);
@@ -265,8 +270,9 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
     MOE_CHECK(launch_gather(P.dtype, dY, o, perm_i, R, P.k, P.N, P.H, st));
     MOE_CHECK(gemm_dh(P.dtype, rg, o, W_down, dh, P.H, P.F, st));
     MOE_CHECK(launch_swiglu_bwd(P.dtype, dh, a, u, h, perm_i, gates, dg, R, P.F, P.N * P.k, st));
-    MOE_CHECK(gemm_wgrad_d(P.dtype, rg.offsets, h, o, dW_down, P.E, P.H, P.F, st));
-    MOE_CHECK(gemm_wgrad_gu(P.dtype, rg.offsets, xp, a, u, dW_gate, dW_up, P.E, P.H, P.F, st));
+    MOE_CHECK(gemm_wgrad_d(P.dtype, rg.offsets, h, o, dW_down, P.E, P.H, P.F, st, wg_init && i == 0));
+    MOE_CHECK(gemm_wgrad_gu(P.dtype, rg.offsets, xp, a, u, dW_gate, dW_up, P.E, P.H, P.F, st,
+                            wg_init && i == 0));
     MOE_CHECK(gemm_dx(P.dtype, rg, a, u, W_gate, W_up, o, P.H, P.F, st));
     MOE_CHECK(launch_combine_bwd(P.dtype, o, wrt, topk_idx, pb.pos, gates, dg, dX, dlogits, P.N,
                                  P.K, i, g.n, P.k, P.E, P.H, st));

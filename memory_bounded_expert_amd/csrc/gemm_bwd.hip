@@ -106,8 +106,10 @@ hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du,
 
 hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, const void* da,
                          const void* du, float* dWg, float* dWu, int E, int H, int F,
-                         hipStream_t st) {
+                         hipStream_t st, bool init) {
+  if (init && dtype != MOE_BF16) return hipErrorInvalidValue;
   Params p{};
+  p.acc_init = init ? 1 : 0;
   p.A = Xp; p.lda = H;
   p.B = da; p.B2 = du; p.ldb = F;
   p.C = dWg; p.C2 = dWu; p.ldc = F; p.c_estride = (int64_t)H * F;
@@ -122,8 +124,10 @@ hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, cons
 }
 
 hipError_t gemm_wgrad_d(int dtype, const int32_t* offsets, const void* hg, const void* dYp,
-                        float* dWd, int E, int H, int F, hipStream_t st) {
+                        float* dWd, int E, int H, int F, hipStream_t st, bool init) {
+  if (init && dtype != MOE_BF16) return hipErrorInvalidValue;
   Params p{};
+  p.acc_init = init ? 1 : 0;
   p.A = hg; p.lda = F;
   p.B = dYp; p.ldb = H;
   p.C = dWd; p.ldc = H; p.c_estride = (int64_t)F * H;

@@ -68,6 +68,9 @@ struct Params {
   const int32_t* a_rows;
   int a_row_div;
   int64_t a_src_rows;
+  // Epi::AccF32, LDS pipeline only: store the tile (C = tile) instead of
+  // accumulating; experts with no rows then store zeros.
+  int acc_init;
 };
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }

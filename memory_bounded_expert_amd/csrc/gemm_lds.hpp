@@ -190,7 +190,7 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
     e = blockIdx.z;
     k_begin = p.offsets[e];
     k_len = p.offsets[e + 1] - (int)k_begin;
-    if (k_len <= 0) return;
+    if (k_len <= 0 && !p.acc_init) return;  // nothing to add
     m0 = blockIdx.x * BM;
     row_end = p.M;
   }
@@ -431,6 +431,7 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
   // unrolled so that every stage index and register set is a compile-time
   // constant.
   constexpr int U = (NS % 2 == 0) ? NS : 2 * NS;
+  if (nk > 0) {  // (an expert with no rows in store mode skips to the epilogue)
   const int last = nk - 1;
 #pragma unroll
   for (int s = 0; s < NS; ++s) issue(min(s, last), s);
@@ -469,6 +470,7 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
     }
   }
   wait_vmcnt<0>();
+  }
 
   if constexpr (EPI == Epi::AccF32) {
     // Weight-gradient accumulation C += tile (fp32 read-modify-write), staged
@@ -510,13 +512,14 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
           const int idx = tid + u * C::THREADS, r = idx / V, c4 = idx - r * V;
-          old[u] = *reinterpret_cast<const f32x4_t*>(Cg + (int64_t)(row0 + r) * p.ldc + n0 + c4 * 4);
+          old[u] = p.acc_init ? f32x4_t{0.f, 0.f, 0.f, 0.f}
+                              : *reinterpret_cast<const f32x4_t*>(Cg + (int64_t)(row0 + r) * p.ldc + n0 + c4 * 4);
         }
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
           const int idx = tid + u * C::THREADS, r = idx / V, c4 = idx - r * V;
           const f32x4_t add = *reinterpret_cast<const f32x4_t*>(stg + r * LD + c4 * 4);
-          *reinterpret_cast<f32x4_t*>(Cg + (int64_t)(row0 + r) * p.ldc + n0 + c4 * 4) = old[u] + add;
+          *reinterpret_cast<f32x4_t*>(Cg + (int64_t)(row0 + r) * p.ldc + n0 + c4 * 4) = p.acc_init ? add : old[u] + add;
         }
       }
     }

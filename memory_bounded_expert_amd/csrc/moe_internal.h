@@ -153,13 +153,14 @@ hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd
 // dXp = da W_gate[e]^T + du W_up[e]^T
 hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du, const void* Wg,
                    const void* Wu, void* dXp, int H, int F, hipStream_t st);
-// dW_gate[e] += Xp_e^T da_e, dW_up[e] += Xp_e^T du_e
+// dW_gate[e] += Xp_e^T da_e, dW_up[e] += Xp_e^T du_e; with init (bf16 only)
+// the products are stored instead (dW = ..., zeros for experts with no rows)
 hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, const void* da,
                          const void* du, float* dWg, float* dWu, int E, int H, int F,
-                         hipStream_t st);
-// dW_down[e] += hg_e^T dYp_e
+                         hipStream_t st, bool init = false);
+// dW_down[e] += hg_e^T dYp_e (init as gemm_wgrad_gu)
 hipError_t gemm_wgrad_d(int dtype, const int32_t* offsets, const void* hg, const void* dYp,
-                        float* dWd, int E, int H, int F, hipStream_t st);
+                        float* dWd, int E, int H, int F, hipStream_t st, bool init = false);
 // logits = X W_r (+ bias), fp32 out
 hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bias, float* logits,
                        int64_t N, int H, int E, hipStream_t st);
