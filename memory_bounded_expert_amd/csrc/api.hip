@@ -37,6 +37,7 @@ Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_d
   L.row_tile = row_tile_for(p);
   L.max_tiles = max_row_tiles((int64_t)(k * ce), (int)E, L.row_tile);
   if (pass == Pass::Forward && need_logits) L.logits = take(N * E * 4);
+  if (pass == Pass::Forward && router_splits(p) > 1) L.rparts = take((size_t)router_splits(p) * N * E * 4);
   L.rank = take(N * k * 4);
   L.blk = take(K * (size_t)L.nblk * E * 4);
   L.offsets = take(K * (E + 1) * 4);
@@ -184,8 +185,10 @@ MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const voi
   int launches = 0;
   (void)hipGetLastError();
 
-  MOE_CHECK(gemm_router(P.dtype, X, W_r, router_bias, lg, P.N, P.H, P.E, st));
-  MOE_CHECK(launch_topk(lg, P.N, P.E, P.k, topk_idx, gates, st));
+  const int rs = router_splits(P);
+  float* rparts = rs > 1 ? (float*)(ws + L.rparts) : nullptr;
+  MOE_CHECK(gemm_router(P.dtype, X, W_r, router_bias, lg, P.N, P.H, P.E, st, rparts, rs));
+  MOE_CHECK(launch_topk(lg, P.N, P.E, P.k, topk_idx, gates, st, rparts, rs, router_bias));
   const PlanBuffers pb = plan_buffers(ws, L, nullptr, nullptr, nullptr);
   MOE_CHECK(launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st));
   launches += 2;
@@ -331,13 +334,15 @@ MOE_API int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   float* lg = (float*)(ws + L.logits);
+  const int rs = router_splits(P);
+  float* rparts = rs > 1 ? (float*)(ws + L.rparts) : nullptr;
   const PlanBuffers pb = plan_buffers(ws, L, nullptr, nullptr, nullptr);
   (void)hipGetLastError();
   hipError_t err = hipSuccess;
   if (stage == MOE_STAGE_ROUTER) {
-    err = gemm_router(P.dtype, X, W_r, router_bias, lg, P.N, P.H, P.E, st);
+    err = gemm_router(P.dtype, X, W_r, router_bias, lg, P.N, P.H, P.E, st, rparts, rs);
   } else if (stage == MOE_STAGE_TOPK) {
-    err = launch_topk(lg, P.N, P.E, P.k, topk_idx, gates, st);
+    err = launch_topk(lg, P.N, P.E, P.k, topk_idx, gates, st, rparts, rs, router_bias);
   } else if (stage == MOE_STAGE_PLAN) {
     err = launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st);
   } else {

@@ -97,7 +97,7 @@ hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd
 }
 
 hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bias, float* logits,
-                       int64_t N, int H, int E, hipStream_t st) {
+                       int64_t N, int H, int E, hipStream_t st, float* parts, int S) {
   if (N == 0) return hipSuccess;
   Params p{};
   p.A = X; p.lda = H;
@@ -105,6 +105,12 @@ hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bi
   p.C = logits; p.ldc = E;
   p.M = (int)N; p.N = E; p.K = H;
   p.bias = bias;
+  if (S > 1) {
+    if (dtype != MOE_BF16 || !parts || H % (64 * S) != 0) return hipErrorInvalidValue;
+    p.C = parts; p.c_estride = N * E; p.Kseg = H / S; p.bias = nullptr;
+    const dim3 grid((unsigned)ceil_div(N, 128), (unsigned)ceil_div(E, 64), (unsigned)S);
+    return launch_lds<Mode::Dense, Shape<128, 64, 2, 4, 64, 1>, false, true, false, false, Epi::F32>(p, grid, st);
+  }
   const dim3 grid((unsigned)ceil_div(N, 128), (unsigned)ceil_div(E, 64));
   return dtype == MOE_BF16
              ? launch_lds<Mode::Dense, Shape<128, 64, 2, 4, 64, 1>, false, true, false, false, Epi::BiasF32>(p, grid, st)

@@ -184,8 +184,11 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
     m0 = tl.y;
     row_end = p.offsets[e + 1];
   } else if constexpr (MODE == Mode::Dense) {
+    // blockIdx.z: K slice of a split product (slice z covers
+    // [z * Kseg, (z + 1) * Kseg) and writes the z-th partial output)
     m0 = blockIdx.x * BM;
     row_end = p.M;
+    if (gridDim.z > 1) k_len = p.Kseg;
   } else {
     e = blockIdx.z;
     k_begin = p.offsets[e];
@@ -201,9 +204,10 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
   k_len = __builtin_amdgcn_readfirstlane(k_len);
   k_begin = (int64_t)__builtin_amdgcn_readfirstlane((int)k_begin);
 
-  const T* Ap = static_cast<const T*>(p.A);
+  const int64_t kslice = (MODE == Mode::Dense && gridDim.z > 1) ? (int64_t)blockIdx.z * p.Kseg : 0;
+  const T* Ap = static_cast<const T*>(p.A) + kslice;
   const T* A2p = static_cast<const T*>(p.A2);
-  const int64_t boff = (MODE == Mode::Rows) ? (int64_t)e * p.b_estride : 0;
+  const int64_t boff = (MODE == Mode::Rows) ? (int64_t)e * p.b_estride : kslice * p.ldb;
   const T* Bp = static_cast<const T*>(p.B) + boff;
   const T* B2p = (DUAL || KCAT) ? static_cast<const T*>(p.B2) + boff : Bp;
   const int nk = (k_len + BK - 1) / BK;
@@ -248,7 +252,7 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
   } else {
     const int64_t rows = (MODE == Mode::Expert) ? (int64_t)k_len : (int64_t)p.K;
     const int64_t kb = (MODE == Mode::Expert) ? k_begin : 0;
-    rB = make_srd(Bp + kb * p.ldb + n0, rows * p.ldb * TS);
+    rB = make_srd(Bp + kb * p.ldb + n0, (MODE == Mode::Dense ? (int64_t)k_len : rows) * p.ldb * TS);
     rB2 = DUAL ? make_srd(B2p + kb * p.ldb + n0, rows * p.ldb * TS) : rB;
   }
 
@@ -549,7 +553,11 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
             static_cast<T*>(p.C3)[o] = f2bf(v1);
           }
         } else if constexpr (EPI == Epi::F32) {
-          static_cast<float*>(p.C)[o] = v0;
+          if constexpr (MODE == Mode::Dense) {  // partial of a split product
+            if (gcol < p.N) static_cast<float*>(p.C)[(int64_t)blockIdx.z * p.c_estride + o] = v0;
+          } else {
+            static_cast<float*>(p.C)[o] = v0;
+          }
         } else if constexpr (EPI == Epi::BiasF32) {
           if (gcol < p.N) static_cast<float*>(p.C)[o] = v0 + (p.bias ? p.bias[gcol] : 0.f);
         }

@@ -45,6 +45,17 @@ inline int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 // The bf16 forward reads each chunk's permuted input rows straight from X
 // inside the gate/up GEMM (no gather kernel, no permuted-input buffer) when X
 // fits one buffer resource's 32-bit offsets.
+// K slices of the bf16 router product: enough that the (N/128) x (E/64)
+// output tiles times the slices fill the chip, each slice a whole number of
+// 64-wide K-tiles and at least 256 deep.
+inline int router_splits(const moe_plan_t& p) {
+  if (p.dtype != MOE_BF16 || p.N == 0) return 1;
+  const int64_t tiles = ceil_div(p.N, 128) * ceil_div(p.E, 64);
+  int s = 1;
+  while (s < 8 && tiles * s < 512 && p.H % (128 * s) == 0 && p.H / (2 * s) >= 256) s *= 2;
+  return s;
+}
+
 inline bool fused_gather(const moe_plan_t& p) {
   return p.dtype == MOE_BF16 && (int64_t)p.N * p.H * 2 <= 0x7FFFFFF0LL;
 }
@@ -66,6 +77,7 @@ inline int row_tile_for(const moe_plan_t& p) {
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct Layout {
   size_t logits = 0;      // [N][E] f32, forward only, when the caller passes none
+  size_t rparts = 0;      // [S][N][E] f32 router partials (split router product)
   size_t rank = 0;        // [N*k] i32  rank of a pair inside its planner block
   size_t blk = 0;         // [K][nblk][E] i32 block counts, then block bases
   size_t offsets = 0;     // [K][E+1] i32
@@ -91,8 +103,11 @@ enum class Pass { Forward, Backward, Debug };
 Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_dgates);
 
 // ---- launchers (all asynchronous on `st`; return the first enqueue error)
+// With parts != nullptr the logits are first summed from the router's S
+// partials (s ascending), plus bias, and written to logits.
 hipError_t launch_topk(const float* logits, int64_t N, int E, int k, int32_t* idx, float* gates,
-                       hipStream_t st);
+                       hipStream_t st, const float* parts = nullptr, int S = 1,
+                       const float* bias = nullptr);
 
 struct PlanBuffers {
   int32_t* rank;
@@ -161,8 +176,11 @@ hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, cons
 // dW_down[e] += hg_e^T dYp_e (init as gemm_wgrad_gu)
 hipError_t gemm_wgrad_d(int dtype, const int32_t* offsets, const void* hg, const void* dYp,
                         float* dWd, int E, int H, int F, hipStream_t st, bool init = false);
-// logits = X W_r (+ bias), fp32 out
+// logits = X W_r (+ bias), fp32 out.  With S > 1 (bf16 only) the product is
+// split over K: parts[s] = X[:, s H/S : (s+1) H/S] W_r[s H/S : (s+1) H/S, :]
+// for s < S ([S][N][E] fp32, no bias), and launch_topk adds them up.
 hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bias, float* logits,
-                       int64_t N, int H, int E, hipStream_t st);
+                       int64_t N, int H, int E, hipStream_t st, float* parts = nullptr,
+                       int S = 1);
 
 }  // namespace moe

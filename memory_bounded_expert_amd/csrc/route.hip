@@ -31,15 +31,20 @@ __device__ __forceinline__ bool beats(float v, int i, float w, int j) {
   return i < j;
 }
 
+// parts != nullptr: the logits are the sum of the router's S K-slice
+// partials (s ascending) plus bias, and are written to `logits` first.
 template <int VPL>
-__global__ __launch_bounds__(kThreads) void topk_gates_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(kThreads) void topk_gates_kernel(float* __restrict__ logits,
                                                               int64_t N, int E, int k,
                                                               int32_t* __restrict__ idx,
-                                                              float* __restrict__ gates) {
+                                                              float* __restrict__ gates,
+                                                              const float* __restrict__ parts,
+                                                              int S,
+                                                              const float* __restrict__ bias) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (t >= N) return;  // whole wave leaves together
-  const float* row = logits + t * E;
+  float* row = logits + t * E;
   float v[VPL];
   uint32_t avail = 0;
 #pragma unroll
@@ -47,7 +52,14 @@ __global__ __launch_bounds__(kThreads) void topk_gates_kernel(const float* __res
     const int e = lane + 64 * j;
     v[j] = 0.f;
     if (e < E) {
-      v[j] = row[e];
+      if (parts) {
+        float acc = parts[t * E + e];
+        for (int s = 1; s < S; ++s) acc += parts[((int64_t)s * N + t) * E + e];
+        v[j] = acc + (bias ? bias[e] : 0.f);
+        row[e] = v[j];
+      } else {
+        v[j] = row[e];
+      }
       avail |= 1u << j;
     }
   }
@@ -95,22 +107,24 @@ __global__ __launch_bounds__(kThreads) void topk_gates_kernel(const float* __res
 
 }  // namespace
 
-hipError_t launch_topk(const float* logits, int64_t N, int E, int k, int32_t* idx, float* gates,
-                       hipStream_t st) {
+hipError_t launch_topk(const float* logits_in, int64_t N, int E, int k, int32_t* idx, float* gates,
+                       hipStream_t st, const float* parts, int S, const float* bias) {
   if (N == 0) return hipSuccess;
+  // written only when summing partials
+  float* logits = const_cast<float*>(logits_in);
   const int per_block = kThreads / 64;
   const dim3 grid((unsigned)((N + per_block - 1) / per_block));
   const int vpl = (E + 63) / 64;
   if (vpl <= 1)
-    topk_gates_kernel<1><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates);
+    topk_gates_kernel<1><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates, parts, S, bias);
   else if (vpl <= 2)
-    topk_gates_kernel<2><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates);
+    topk_gates_kernel<2><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates, parts, S, bias);
   else if (vpl <= 4)
-    topk_gates_kernel<4><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates);
+    topk_gates_kernel<4><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates, parts, S, bias);
   else if (vpl <= 8)
-    topk_gates_kernel<8><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates);
+    topk_gates_kernel<8><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates, parts, S, bias);
   else
-    topk_gates_kernel<16><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates);
+    topk_gates_kernel<16><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates, parts, S, bias);
   return hipGetLastError();
 }
 
