@@ -56,13 +56,29 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__
     float acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-    for (int s = 0; s < k; ++s) {
-      const int64_t r = pos[t * k + s];
-      const float g = gates[t * k + s];
-      float v[EPC];
-      unpack16(reinterpret_cast<const u32x4_t*>(O + r * H)[c], v, T());
+    // slots in batches of SB: all of a batch's row loads are issued before
+    // any is consumed; the sum still runs in slot order
+    constexpr int SB = 8;
+    for (int s0 = 0; s0 < k; s0 += SB) {
+      u32x4_t raw[SB];
+      float g[SB];
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[e] = fmaf(g, v[e], acc[e]);
+      for (int u = 0; u < SB; ++u) {
+        if (s0 + u < k) {
+          const int64_t r = pos[t * k + s0 + u];
+          g[u] = gates[t * k + s0 + u];
+          raw[u] = reinterpret_cast<const u32x4_t*>(O + r * H)[c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        if (s0 + u < k) {
+          float v[EPC];
+          unpack16(raw[u], v, T());
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[e] = fmaf(g[u], v[e], acc[e]);
+        }
+      }
     }
     reinterpret_cast<u32x4_t*>(Y + t * H)[c] = pack16(acc, T());
   }

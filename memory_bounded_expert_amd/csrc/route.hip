@@ -105,6 +105,64 @@ __global__ __launch_bounds__(kThreads) void topk_gates_kernel(float* __restrict_
   }
 }
 
+// E <= 64: lane e holds expert e's logit and computes its rank directly --
+// the number of experts that beat it under the same order (logit descending,
+// index ascending, IEEE comparison) -- from the wave's 64 logits staged in
+// LDS.  Lanes with rank < k own slot `rank`.  The gate denominator is a wave
+// sum over the selected lanes.
+__global__ __launch_bounds__(kThreads) void topk_rank_kernel(float* __restrict__ logits, int64_t N,
+                                                             int E, int k,
+                                                             int32_t* __restrict__ idx,
+                                                             float* __restrict__ gates,
+                                                             const float* __restrict__ parts,
+                                                             int S,
+                                                             const float* __restrict__ bias) {
+  __shared__ float sv[kThreads / 64][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + w;
+  if (t >= N) return;  // whole wave leaves together; no block barrier below
+  float* row = logits + t * E;
+  const bool valid = lane < E;
+  float v = -INFINITY;
+  if (valid) {
+    if (parts) {
+      float acc = parts[t * E + lane];
+      for (int s = 1; s < S; ++s) acc += parts[((int64_t)s * N + t) * E + lane];
+      v = acc + (bias ? bias[lane] : 0.f);
+      row[lane] = v;
+    } else {
+      v = row[lane];
+    }
+  }
+  sv[w][lane] = v;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes done (lgkmcnt 0)
+  int rank = 0;
+  float top = -INFINITY;
+#pragma unroll
+  for (int j4 = 0; j4 < 16; ++j4) {
+    const float4 q = *reinterpret_cast<const float4*>(&sv[w][4 * j4]);
+    const float o[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int j = 4 * j4 + m;
+      if (j < E) {
+        top = fmaxf(top, o[m]);
+        rank += (o[m] > v || (!(v > o[m]) && j < lane)) ? 1 : 0;
+      }
+    }
+  }
+  const bool sel = valid && rank < k;
+  float ex = sel ? expf(v - top) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if (sel) {
+    idx[t * k + rank] = lane;
+    gates[t * k + rank] = ex / sum;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float* logits_in, int64_t N, int E, int k, int32_t* idx, float* gates,
@@ -115,6 +173,10 @@ hipError_t launch_topk(const float* logits_in, int64_t N, int E, int k, int32_t*
   const int per_block = kThreads / 64;
   const dim3 grid((unsigned)((N + per_block - 1) / per_block));
   const int vpl = (E + 63) / 64;
+  if (vpl <= 1) {
+    topk_rank_kernel<<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates, parts, S, bias);
+    return hipGetLastError();
+  }
   if (vpl <= 1)
     topk_gates_kernel<1><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates, parts, S, bias);
   else if (vpl <= 2)
