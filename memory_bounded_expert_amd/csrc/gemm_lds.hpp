@@ -28,6 +28,8 @@
 // per-lane load offsets, so the LDS writes of a wave stay one contiguous KiB.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "gemm_kernel.hpp"  // Mode, Epi, Params, make_rsrc, wave_uniform
 #include "moe_internal.h"
@@ -525,6 +527,66 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
           const f32x4_t add = *reinterpret_cast<const f32x4_t*>(stg + r * LD + c4 * 4);
           *reinterpret_cast<f32x4_t*>(Cg + (int64_t)(row0 + r) * p.ldc + n0 + c4 * 4) = p.acc_init ? add : old[u] + add;
         }
+      }
+    }
+    return;
+  }
+
+  if constexpr (MODE == Mode::Rows && (EPI == Epi::Store || EPI == Epi::SwiGLU ||
+                                      EPI == Epi::SwiGLUSave || EPI == Epi::F32)) {
+    // Row-grouped outputs go out through LDS: each wave parks its fragment
+    // values (computed exactly as below) in the free operand stages, slab by
+    // slab of wave row slices, and the work-group then writes the slab with
+    // 16-byte, row-contiguous stores, skipping rows past the segment end.
+    // Rows are padded by 16 bytes (fragment row groups land in distinct
+    // banks; 16-byte reads stay aligned).
+    auto stage_store = [&](auto* Cbase, auto value) __attribute__((always_inline)) {
+      using OT = typename std::remove_pointer<decltype(Cbase)>::type;
+      constexpr int ES = (int)sizeof(OT);
+      constexpr int LD = BN + 16 / ES;       // padded row, elements
+      constexpr int VE = 16 / ES;            // elements per 16-byte vector
+      constexpr int V = BN / VE;             // vectors per tile row
+      constexpr int SLAB_FIT = (NS * C::STAGE) / (WM * LD * ES);
+      constexpr int SLAB = SLAB_FIT >= S::WGM ? S::WGM : (SLAB_FIT >= 2 && S::WGM % 2 == 0 ? 2 : 1);
+      constexpr int SR = SLAB * WM;
+      static_assert(SR * LD * ES <= NS * C::STAGE, "output staging must fit the LDS stages");
+      static_assert(S::WGM % SLAB == 0, "slabs of whole wave row slices");
+      OT* stg = reinterpret_cast<OT*>(smem);
+#pragma unroll
+      for (int sl = 0; sl < S::WGM / SLAB; ++sl) {
+        lds_barrier();  // previous users of the LDS are done
+        if (wm / SLAB == sl) {
+          const int r0 = (wm - sl * SLAB) * WM;
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                stg[(r0 + i * 16 + 4 * lg + q) * LD + wn * WN + j * 16 + l16] = value(i, j, q);
+        }
+        lds_barrier();
+        const int row0 = m0 + sl * SR;
+        for (int idx = tid; idx < SR * V; idx += C::THREADS) {
+          const int r = idx / V, c = idx - r * V;
+          if (row0 + r >= row_end) break;  // rows ascend with idx
+          *reinterpret_cast<u32x4_t*>(Cbase + (int64_t)(row0 + r) * p.ldc + n0 + c * VE) =
+              *reinterpret_cast<const u32x4_t*>(stg + r * LD + c * VE);
+        }
+      }
+    };
+    if constexpr (EPI == Epi::Store) {
+      stage_store(static_cast<T*>(p.C), [&](int i, int j, int q) { return f2bf(acc[0][i][j][q]); });
+    } else if constexpr (EPI == Epi::F32) {
+      stage_store(static_cast<float*>(p.C), [&](int i, int j, int q) { return acc[0][i][j][q]; });
+    } else {
+      stage_store(static_cast<T*>(p.C), [&](int i, int j, int q) {
+        const float v0 = acc[0][i][j][q], v1 = acc[NB - 1][i][j][q];
+        return f2bf(__fdividef(v0, 1.f + __expf(-v0)) * v1);
+      });
+      if constexpr (EPI == Epi::SwiGLUSave) {
+        stage_store(static_cast<T*>(p.C2), [&](int i, int j, int q) { return f2bf(acc[0][i][j][q]); });
+        stage_store(static_cast<T*>(p.C3), [&](int i, int j, int q) { return f2bf(acc[NB - 1][i][j][q]); });
       }
     }
     return;
