@@ -1,8 +1,11 @@
 // Grouped GEMM on gfx950 MFMA ("Grouped GEMM organizes computation by
 // expert-aggregated batches": "Training Trillion-Parameter MoE ...",
-// section 3.3).
+// section 3.3): the definitions shared by both GEMM kernels (modes,
+// epilogues, parameters, buffer resources, MFMA wrappers) and the
+// register-staged kernel that runs the fp32 configuration.  bf16 products
+// run the LDS-pipeline kernel of gemm_lds.hpp.
 //
-// One kernel template serves every contraction of the layer:
+// The kernel templates serve every contraction of the layer:
 //   Mode::Rows    C[rows of expert e] = A[rows] . B[e]   (row-grouped: the
 //                 permuted buffer's expert segments; M-tiles come from the
 //                 planner's per-chunk tile list, so no host sync is needed)

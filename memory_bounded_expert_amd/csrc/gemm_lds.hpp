@@ -1,21 +1,22 @@
 // bf16 grouped GEMM on gfx950 with an LDS-only operand pipeline.
 //
 // Same contraction modes as gemm_kernel.hpp (Rows: expert segments of a
-// chunk, M-tiles from the planner's device-side list; Dense: router; Expert:
-// weight gradients), same 2 x 2 wave grid of v_mfma_f32_16x16x32_bf16 with
-// fp32 accumulation, and the same K order for every output element -- so a
-// row's result does not depend on which rows share its tile.  What changes
-// is how operands reach the MFMAs:
+// chunk, M-tiles from the planner's device-side list; Dense: router, optionally
+// split over K; Expert: weight gradients), v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation on a WGM x WGN grid of waves (Shape below), and the same K
+// order for every output element -- so a row's result does not depend on
+// which rows share its tile.  How operands reach the MFMAs:
 //
 //  * Every operand tile goes from HBM straight into LDS with buffer loads
 //    that write LDS (16 bytes per lane; lane L of a wave lands at base +
-//    16 L).  No staging registers, so NS = 3..4 LDS stages fit and two to
-//    three K-tiles are in flight per work-group while the MFMAs consume the
-//    current one.  Loads past a tile's valid rows (buffer resource bounds)
-//    write zeros.
+//    16 L).  No staging registers, so 3 to 6 LDS stages fit and NS-1 K-tiles
+//    are in flight per work-group while the MFMAs consume the current one.
+//    Loads past a tile's valid rows (buffer resource bounds) write zeros.
+//    The bf16 forward's gate/up product can take its A rows straight from X
+//    through the chunk's permutation (Params::a_rows).
 //  * K-contiguous operands (activation rows; weights in the transposed
-//    products) are stored as rows of 8 chunks of 16 bytes, chunk c of row r
-//    at slot c ^ (r & 7), and read with ds_read_b128.
+//    products) are stored as rows of BK/8 chunks of 16 bytes with a
+//    row-dependent XOR swizzle of the chunk index, read with ds_read_b128.
 //  * M/N-contiguous operands (weights in the forward products; activations
 //    in the weight gradients) stay M/N-contiguous in LDS and are read with
 //    ds_read_b64_tr_b16: in each 16-lane group, lanes 4j..4j+3 address row j
@@ -104,10 +105,6 @@ struct Shape {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_;
   static constexpr int WG_PER_CU = WG_PER_CU_;
 };
-// streaming shape: 8 waves of 64 x 64, BK 64, one work-group per CU
-template <int BN> using Stream = Shape<128, BN, 2, 4, 64, 1>;
-// compute shape: 2 waves of 128 x 128, BK 32, two work-groups per CU
-template <int BN> using Compute = Shape<128, BN, 1, 2, 32, 2>;
 
 template <class S, bool DUAL>
 struct LdsCfg {

@@ -145,7 +145,7 @@ hipError_t launch_dwr(int dtype, const void* Xp, const int32_t* perm_chunk, cons
                       const float* dlogits, float* dWr, int k, int E, int H, int64_t N,
                       hipStream_t st);
 
-// GEMMs (see gemm.hip for the tile scheme).
+// GEMMs (tile schemes: gemm_lds.hpp for bf16, gemm_kernel.hpp for fp32).
 struct RowsGeom {
   const int2* tiles;
   const int32_t* tile_count;
