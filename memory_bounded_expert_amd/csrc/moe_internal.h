@@ -42,9 +42,6 @@ inline ChunkGeom chunk_geom(int64_t N, int64_t K, int64_t k, int64_t i) {
 
 inline int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
-// The bf16 forward reads each chunk's permuted input rows straight from X
-// inside the gate/up GEMM (no gather kernel, no permuted-input buffer) when X
-// fits one buffer resource's 32-bit offsets.
 // K slices of the bf16 router product: enough that the (N/128) x (E/64)
 // output tiles times the slices fill the chip, each slice a whole number of
 // 64-wide K-tiles and at least 256 deep.
@@ -56,6 +53,9 @@ inline int router_splits(const moe_plan_t& p) {
   return s;
 }
 
+// The bf16 forward reads each chunk's permuted input rows straight from X
+// inside the gate/up GEMM (no gather kernel, no permuted-input buffer) when X
+// fits one buffer resource's 32-bit offsets.
 inline bool fused_gather(const moe_plan_t& p) {
   return p.dtype == MOE_BF16 && (int64_t)p.N * p.H * 2 <= 0x7FFFFFF0LL;
 }
