@@ -141,6 +141,35 @@ __device__ __forceinline__ void transpose_block(const u32x4_t* in, u32x4_t* out,
     out[c] = u32x4_t{word(in[0], c), word(in[1], c), word(in[2], c), word(in[3], c)};
 }
 
+// Work-group ids are handed out round-robin over the 8 XCDs (id mod 8), each
+// with its own L2.  Renumbers id L of a grid of `total` work-groups so that
+// every XCD runs one contiguous range of the new ids (a bijection on
+// [0, total)).
+__device__ __forceinline__ int xcd_contiguous(int L, int total) {
+  const int xcd = L & 7, slot = L >> 3;
+  const int q = total >> 3, r = total & 7;
+  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// Weight-gradient grids are (M-tiles, N-tiles, experts).  The tiles of one
+// expert all read that expert's activation rows, so they go to one XCD (the
+// renumbered ids run expert by expert, N-tile fastest) and the rows are
+// fetched into one L2 instead of eight.
+struct ExpertTile {
+  int e, mt, nt;
+};
+__device__ __forceinline__ ExpertTile expert_tile() {
+  const int gx = gridDim.x, gy = gridDim.y, per = gx * gy;
+  const int L = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int lid = xcd_contiguous(L, per * gridDim.z);
+  ExpertTile t;
+  t.e = lid / per;
+  const int rem = lid - t.e * per;
+  t.mt = rem / gy;
+  t.nt = rem - t.mt * gy;
+  return t;
+}
+
 template <typename T, Mode MODE, int BM, int BN, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI,
           int STAGES = 1>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
@@ -183,9 +212,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
     const int total = *p.tile_count * p.ntiles;
     const int L = blockIdx.x;
     if (L >= total) return;
-    const int xcd = L & 7, slot = L >> 3;
-    const int q = total >> 3, r = total & 7;
-    const int lid = xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+    const int lid = xcd_contiguous(L, total);
     const int mt = lid / p.ntiles;
     n0 = (lid - mt * p.ntiles) * BN;
     const int2 tl = p.tiles[mt];
@@ -196,11 +223,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
     m0 = blockIdx.x * BM;
     row_end = p.M;
   } else {
-    e = blockIdx.z;
+    const ExpertTile t = expert_tile();
+    e = t.e;
     k_begin = p.offsets[e];
     k_len = p.offsets[e + 1] - (int)k_begin;
     if (k_len <= 0) return;
-    m0 = blockIdx.x * BM;
+    m0 = t.mt * BM;
+    n0 = t.nt * BN;
     row_end = p.M;
   }
   // The tile descriptor is the same for the whole work-group; make that

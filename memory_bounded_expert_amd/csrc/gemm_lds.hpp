@@ -91,6 +91,31 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Orders one wave's LDS writes before its later LDS reads of other lanes'
+// data (and those reads before later writes): the DS unit executes a wave's
+// instructions in order, so waiting for this wave's own LDS operations
+// (lgkmcnt 0) and keeping the compiler from moving memory operations across
+// is enough; no work-group barrier.
+__device__ __forceinline__ void wave_lds_sync() {
+  constexpr int kWaitLgkm0 = 0xC07F;  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Rows per slice of a wave's WM x WN accumulator block in the weight-gradient
+// read-modify-write: the largest power-of-two share of WM (at least one
+// fragment row) whose padded rows fit the wave's LDS share and that gives each
+// lane at most 8 vectors of 16 bytes, so two slices' old values fit in
+// registers beside the accumulators.
+template <int WM, int LD, int VW, int PWB>
+constexpr int acc_slice_rows() {
+  int sr = WM;
+  while (sr > 16 && (sr * LD * 4 > PWB || sr * VW > 8 * 64)) sr /= 2;
+  return sr;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -169,13 +194,11 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
   int64_t k_begin = 0;
   int k_len = p.K;
   if constexpr (MODE == Mode::Rows) {
-    // XCD-aware renumbering of the 1-D grid (see gemm_kernel.hpp)
+    // XCD-aware renumbering of the 1-D grid (xcd_contiguous)
     const int total = *p.tile_count * p.ntiles;
     const int L = blockIdx.x;
     if (L >= total) return;
-    const int xcd = L & 7, slot = L >> 3;
-    const int q = total >> 3, r = total & 7;
-    const int lid = xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+    const int lid = xcd_contiguous(L, total);
     const int mt = lid / p.ntiles;
     n0 = (lid - mt * p.ntiles) * BN;
     const int2 tl = p.tiles[mt];
@@ -189,11 +212,13 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
     row_end = p.M;
     if (gridDim.z > 1) k_len = p.Kseg;
   } else {
-    e = blockIdx.z;
+    const ExpertTile t = expert_tile();
+    e = t.e;
     k_begin = p.offsets[e];
     k_len = p.offsets[e + 1] - (int)k_begin;
     if (k_len <= 0 && !p.acc_init) return;  // nothing to add
-    m0 = blockIdx.x * BM;
+    m0 = t.mt * BM;
+    n0 = t.nt * BN;
     row_end = p.M;
   }
   e = __builtin_amdgcn_readfirstlane(e);
@@ -476,55 +501,66 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
   }
 
   if constexpr (EPI == Epi::AccF32) {
-    // Weight-gradient accumulation C += tile (fp32 read-modify-write), staged
-    // through LDS so that HBM sees 16-byte, row-contiguous loads and stores
-    // instead of the fragments' 4-byte scatter.  Each element is still
-    // old + new in one fp32 add.  The operand stages are free: every load has
-    // landed (vmcnt 0 above) and the barrier orders every wave's last fragment
-    // reads before the overwrite.  The tile goes through in slabs of SLAB wave
-    // row slices (as many as the stages hold); rows are padded by 4 floats so
-    // the four row groups of a fragment land in distinct banks.
-    constexpr int LD = BN + 4;
-    constexpr int V = BN / 4;  // 16-byte vectors per tile row
-    constexpr int SLAB_FIT = (NS * C::STAGE) / (WM * LD * 4);
-    constexpr int SLAB = SLAB_FIT >= S::WGM ? S::WGM : (SLAB_FIT >= 2 && S::WGM % 2 == 0 ? 2 : 1);
-    constexpr int SR = SLAB * WM;  // rows per slab
-    constexpr int PER = SR * V / C::THREADS;
-    static_assert(SR * LD * 4 <= NS * C::STAGE, "accumulator staging must fit the LDS stages");
-    static_assert(S::WGM % SLAB == 0 && (SR * V) % C::THREADS == 0, "slab must split over the threads");
-    float* stg = reinterpret_cast<float*>(smem);
-#pragma unroll
-    for (int g = 0; g < NB; ++g) {
+    // Weight-gradient accumulation C += tile (fp32 read-modify-write).  Each
+    // wave moves its own WM x WN block through a private share of the free
+    // operand stages, SR rows at a time, so that HBM sees 16-byte,
+    // row-contiguous loads and stores instead of the fragments' 4-byte
+    // scatter.  The old values of slice s+1 are requested before slice s is
+    // added and stored, so the read latency overlaps the previous slice's
+    // work.  Each element is still old + new in one fp32 add (the product
+    // alone when acc_init).  The operand stages are free once every wave's
+    // last fragment reads are done (the barrier); after it each wave touches
+    // only its own share, so no further work-group barriers.  Rows are
+    // padded by 4 floats so the four row groups of a fragment land in
+    // distinct banks.
+    constexpr int LD = WN + 4;
+    constexpr int VW = WN / 4;                       // 16-byte vectors per wave row
+    constexpr int PWB = NS * C::STAGE / C::WAVES;    // LDS bytes per wave
+    constexpr int SR = acc_slice_rows<WM, LD, VW, PWB>();
+    constexpr int NSL = WM / SR;                     // slices per operand group
+    constexpr int NSUB = NB * NSL;
+    constexpr int PER = SR * VW / 64;                // vectors per lane per slice
+    constexpr int FS = SR / 16;                      // fragment rows per slice
+    static_assert(SR % 16 == 0 && WM % SR == 0, "slices of whole fragment rows");
+    static_assert(SR * LD * 4 <= PWB, "accumulator slice must fit the wave's LDS share");
+    static_assert((SR * VW) % 64 == 0 && PER <= 8, "slice must split over the lanes");
+    float* stg = reinterpret_cast<float*>(smem + wave * PWB);
+    const int rw0 = m0 + wm * WM, cw0 = n0 + wn * WN;  // this wave's block
+    auto gptr = [&](int s, int u) __attribute__((always_inline)) {
+      const int g = s / NSL, sl = s - g * NSL;
+      const int idx = lane + u * 64, r = idx / VW, c4 = idx - r * VW;
       float* Cg = static_cast<float*>(g == 0 ? p.C : p.C2) + (int64_t)e * p.c_estride;
+      return reinterpret_cast<f32x4_t*>(Cg + (int64_t)(rw0 + sl * SR + r) * p.ldc + cw0 + c4 * 4);
+    };
+    const bool accumulate = !p.acc_init;
+    f32x4_t old[2][PER];
+    if (accumulate) {
 #pragma unroll
-      for (int sl = 0; sl < S::WGM / SLAB; ++sl) {
-        lds_barrier();  // previous users of the LDS are done
-        if (wm / SLAB == sl) {
-          const int r0 = (wm - sl * SLAB) * WM;
+      for (int u = 0; u < PER; ++u) old[0][u] = *gptr(0, u);
+    }
+    lds_barrier();  // every wave's last fragment reads are done
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
+    for (int s = 0; s < NSUB; ++s) {
+      const int g = s / NSL, sl = s - g * NSL;
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+      for (int i = 0; i < FS; ++i)
 #pragma unroll
-              for (int q = 0; q < 4; ++q)
-                stg[(r0 + i * 16 + 4 * lg + q) * LD + wn * WN + j * 16 + l16] = acc[g][i][j][q];
-        }
-        lds_barrier();
-        const int row0 = m0 + sl * SR;
-        f32x4_t old[PER];
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          const int idx = tid + u * C::THREADS, r = idx / V, c4 = idx - r * V;
-          old[u] = p.acc_init ? f32x4_t{0.f, 0.f, 0.f, 0.f}
-                              : *reinterpret_cast<const f32x4_t*>(Cg + (int64_t)(row0 + r) * p.ldc + n0 + c4 * 4);
-        }
+          for (int q = 0; q < 4; ++q)
+            stg[(i * 16 + 4 * lg + q) * LD + j * 16 + l16] = acc[g][sl * FS + i][j][q];
+      wave_lds_sync();
+      if (accumulate && s + 1 < NSUB) {
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          const int idx = tid + u * C::THREADS, r = idx / V, c4 = idx - r * V;
-          const f32x4_t add = *reinterpret_cast<const f32x4_t*>(stg + r * LD + c4 * 4);
-          *reinterpret_cast<f32x4_t*>(Cg + (int64_t)(row0 + r) * p.ldc + n0 + c4 * 4) = p.acc_init ? add : old[u] + add;
-        }
+        for (int u = 0; u < PER; ++u) old[(s + 1) & 1][u] = *gptr(s + 1, u);
       }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int idx = lane + u * 64, r = idx / VW, c4 = idx - r * VW;
+        const f32x4_t add = *reinterpret_cast<const f32x4_t*>(stg + r * LD + c4 * 4);
+        *gptr(s, u) = accumulate ? old[s & 1][u] + add : add;
+      }
+      wave_lds_sync();  // this slice's reads are done before the next slice's writes
     }
     return;
   }

@@ -210,3 +210,17 @@ def test_large_row_tile_bf16():
     assert plan.K == 3 and plan.c_eff == 534
     assert wl.k * plan.c_eff >= 96 * wl.E and wl.H % 128 == 0 and wl.F % 128 == 0
     run_workload(wl.name, full=False, wl=wl, reduced=(wl.N, wl.c))
+
+
+# Experts spanning several full 256-row tiles: K = 2 chunks of 1024 tokens
+# give about 512 rows per expert per chunk (two or three M-tiles each), and
+# the unchunked comparison run about 1024 (four or five).
+GROUPED = datagen.WORKLOADS["train_bf16"].with_(
+    name="grouped_tiles_bf16", N=2048, H=256, E=8, k=4, F=384, c=1024, K_max=16)
+
+
+def test_grouped_row_tiles_bf16():
+    wl = GROUPED
+    plan = plan_for(wl)
+    assert plan.K == 2 and plan.c_eff == 1024
+    run_workload(wl.name, full=False, wl=wl, reduced=(wl.N, wl.c))
