@@ -177,3 +177,76 @@ class Inputs:
         if self.Wg is not None:
             return self.to_f64(self.Wg[e]), self.to_f64(self.Wu[e]), self.to_f64(self.Wd[e])
         return tuple(self.to_f64(a) for a in self.expert_storage(e))
+
+
+# ---------------------------------------------------------------------------
+# Vocabulary projection with cross-entropy, computed over vocabulary strips.
+# Tensor ids of its own streams; W is drawn in blocks of CE_W_BLOCK rows, one
+# stream per block, so any block can be regenerated alone.
+
+TID_CE_X = 11
+TID_CE_W = 12
+TID_CE_T = 13
+TID_CE_IGN = 14
+CE_W_BLOCK = 4096
+
+
+@dataclasses.dataclass(frozen=True)
+class CeWorkload:
+    name: str
+    N: int        # tokens
+    H: int        # hidden width
+    V: int        # vocabulary
+    v_chunk: int  # vocabulary strip width
+    dtype: str    # "bf16"
+    x_std: float
+    w_std: float
+    ignore_frac: float = 0.0  # fraction of tokens whose target is ignored (-100)
+    seed: int = 0
+
+    def with_(self, **kw) -> "CeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+CE_WORKLOADS: Dict[str, CeWorkload] = {
+    # the vocabulary-projection shape of the bounded-streaming measurements
+    # (H 7168, V 200,000) on one GPU, 8192 tokens, strips of 8192 entries
+    "vocab_bf16": CeWorkload("vocab_bf16", N=8192, H=7168, V=200_000, v_chunk=8192,
+                             dtype="bf16", x_std=1.0, w_std=0.02),
+    # small case the oracle runs whole: ragged last strip and ragged tiles
+    "vocab_small_bf16": CeWorkload("vocab_small_bf16", N=777, H=512, V=20_000, v_chunk=4096,
+                                   dtype="bf16", x_std=1.0, w_std=0.05, ignore_frac=0.05),
+}
+
+
+class CeInputs:
+    """Host copies of one CE workload's inputs: X [N, H] and W [V, H] as bf16
+    bit patterns (uint16), targets [N] int32 uniform over the vocabulary (a
+    seeded fraction set to -100, the ignored marker), dloss [N] fp32 = 1/N
+    (the upstream gradient of the mean loss)."""
+
+    def __init__(self, wl: CeWorkload, N: Optional[int] = None, progress=None):
+        self.wl = wl
+        self.N = wl.N if N is None else N
+        s = wl.seed
+        self.X = f32_to_bf16_bits(normal_f32((self.N, wl.H), wl.x_std, s, TID_CE_X))
+        self.W = np.empty((wl.V, wl.H), np.uint16)
+        for b0 in range(0, wl.V, CE_W_BLOCK):
+            self.W[b0:b0 + CE_W_BLOCK] = self.w_block(b0 // CE_W_BLOCK)
+            if progress is not None and (b0 // CE_W_BLOCK) % 16 == 15:
+                progress(f"{wl.name}: W rows {b0 + CE_W_BLOCK}/{wl.V} drawn")
+        t = rng(s, TID_CE_T).integers(0, wl.V, self.N, dtype=np.int64)
+        if wl.ignore_frac > 0:
+            ign = rng(s, TID_CE_IGN).random(self.N) < wl.ignore_frac
+            t[ign] = -100
+        self.targets = t.astype(np.int32)
+        self.dloss = np.full(self.N, 1.0 / max(self.N, 1), np.float32)
+
+    def w_block(self, blk: int) -> np.ndarray:
+        wl = self.wl
+        rows = min(CE_W_BLOCK, wl.V - blk * CE_W_BLOCK)
+        return f32_to_bf16_bits(normal_f32((rows, wl.H), wl.w_std, wl.seed, TID_CE_W, blk))
+
+    @staticmethod
+    def to_f64(a: np.ndarray) -> np.ndarray:
+        return bf16_bits_to_f32(a).astype(np.float64)

@@ -26,3 +26,16 @@ from .moe_oracle import (  # noqa: F401
     logit_error_bound,
     dispatch_bound_bytes,
 )
+
+from .ce_oracle import (  # noqa: F401,E402
+    ce_strips,
+    strip_bound_bytes,
+    ce_logits,
+    ce_forward,
+    ce_fold_strips,
+    ce_dlogits,
+    ce_backward,
+    ce_forward_tokens,
+    ce_backward_tokens,
+    ce_backward_tokens_rows,
+)
