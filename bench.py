@@ -14,6 +14,11 @@ Prints one JSON line on stdout (everything else goes to stderr):
   roofline = the dominant kernel against its roof (HBM or bf16 MFMA), from
              HIP events around re-launches of that kernel on the layer's stream,
   cpu_baseline = the fp64 oracle on a bounded sample of the same workload.
+
+--workload vocab_bf16 (or vocab_small_bf16) benchmarks the vocabulary
+projection with cross-entropy over vocabulary strips instead: one step = the
+forward (per-token loss and log-normaliser) and backward (dX, dW) of 8192
+tokens over H=7168, V=200,000 in strips of 8192 entries; value = tokens/s.
 """
 
 from __future__ import annotations
@@ -89,6 +94,168 @@ def stage_work(stage, wl, b, n_i, R_i, E_i):
     raise KeyError(stage)
 
 
+def cce_stage_work(stage, N, H, w):
+    """Algorithmic (bytes, flops) of one launch of a vocabulary-strip
+    cross-entropy stage on a strip of w vocabulary entries (bf16 X, W and
+    logit gradient; fp32 statistics, dX running sum and dW)."""
+    gemm = 2.0 * N * H * w
+    x, ws, g = N * H * 2, w * H * 2, N * w * 2
+    if stage == "logits":  # X, the strip of W, slice statistics out
+        return x + ws + N * (w // 128) * 8 + N * 4, gemm
+    if stage == "fold":  # slice statistics in, running state
+        return N * (w // 128) * 8 + N * 16, 0.0
+    if stage == "grad":  # X, the strip of W, logit gradient out
+        return x + ws + g + N * 12, gemm
+    if stage == "dx":  # logit gradient, the strip of W, dX running sum read and written
+        return g + ws + N * H * 8, gemm
+    if stage == "dw":  # logit gradient, X, the strip's dW rows out
+        return g + x + w * H * 4, gemm
+    raise KeyError(stage)
+
+
+def cce_main(args, datagen, np, torch, B):
+    """One step = forward + backward of the vocabulary projection with
+    cross-entropy over vocabulary strips, on one batch of N tokens."""
+    dev = torch.device("cuda:0")
+    wl = datagen.CE_WORKLOADS[args.workload]
+    log(f"generating {wl.name} inputs")
+    inp = datagen.CeInputs(wl)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    X, W = bf(inp.X), bf(inp.W)
+    t = torch.from_numpy(inp.targets).to(dev)
+    dloss = torch.from_numpy(inp.dloss).to(dev)
+    N, H, V, vc = wl.N, wl.H, wl.V, wl.v_chunk
+    plan = B.cce_plan(N, H, V, vc)
+    stream = torch.cuda.current_stream(dev)
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty_like(loss)
+    dX = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    wsf = B.workspace(plan, "fwd", dev)
+    wsb = B.workspace(plan, "bwd", dev)
+    log(f"plan: S={plan.S} strips of {vc}, workspace fwd {plan.fwd_workspace_bytes} B, "
+        f"bwd {plan.bwd_workspace_bytes} B")
+
+    def fwd():
+        B.cce_forward(plan, X, W, t, loss=loss, lse=lse, ws=wsf, stream=stream)
+
+    def bwd():
+        B.cce_backward(plan, X, W, t, lse, dloss, dX=dX, dW=dW, ws=wsb, stream=stream)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, k):
+        e0, e1 = ev(), ev()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    w0 = time.perf_counter()
+    ms = timed(lambda: (fwd(), bwd()), args.steps)
+    wall = (time.perf_counter() - w0) / args.steps * 1e3
+    peak_extra = torch.cuda.max_memory_allocated(dev) - mem0
+    ms_f = timed(fwd, args.steps)
+    log(f"forward+backward: {ms:.3f} ms/step ({N / (ms / 1e3):.4g} tokens/s); forward {ms_f:.3f} ms")
+
+    # per-kernel: re-launch each stage of each strip in pipeline order
+    fwd()
+    torch.cuda.synchronize()
+    stages = {}
+    strips = [min(vc, V - s * vc) for s in range(plan.S)]
+    for group, names in (("fwd", ("logits", "fold")), ("bwd", ("grad", "dx", "dw"))):
+        if group == "bwd":
+            bwd()
+        marks = {n: [] for n in names}
+        for _ in range(args.stage_reps):
+            for si in range(plan.S):
+                for n in names:
+                    e0, e1 = ev(), ev()
+                    e0.record(stream)
+                    B.cce_debug_stage(plan, n, si, X, W, t, loss, lse, dloss, dX, dW,
+                                      wsf if group == "fwd" else wsb, stream=stream)
+                    e1.record(stream)
+                    marks[n].append((e0, e1))
+        torch.cuda.synchronize()
+        for n in names:
+            us = float(np.mean([a.elapsed_time(b_) for a, b_ in marks[n]])) * 1e3
+            byts = float(np.mean([cce_stage_work(n, N, H, w)[0] for w in strips]))
+            flops = float(np.mean([cce_stage_work(n, N, H, w)[1] for w in strips]))
+            rec = {"us_per_launch": round(us, 2), "launches_per_step": plan.S,
+                   "GB_per_s": round(byts / us / 1e3, 1), "alg_bytes_per_launch": int(byts)}
+            if flops:
+                rec["TFLOP_per_s"] = round(flops / us / 1e6, 1)
+                rec["mfma_frac"] = round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4)
+                rec["alg_flops_per_launch"] = int(flops)
+            stages[n] = rec
+            log(f"  {n:7s} {rec}")
+    # the timed outputs are reproduced by a fresh forward + backward
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    dom = max(stages, key=lambda n: stages[n]["us_per_launch"])
+    d = stages[dom]
+    roof = {"bound": "mfma", "achieved": d["TFLOP_per_s"], "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(d["TFLOP_per_s"] / BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(wl.name, dom), "kernel": dom}
+    gemm_flops = 8.0 * N * H * V
+    out = {
+        "metric": "tokens/s (forward+backward) of the vocabulary projection with cross-entropy "
+                  "at bounded strip memory",
+        "value": round(N / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normals, bf16-rounded; uniform targets)",
+        "config": {"workload": wl.name, "N": N, "H": H, "V": V, "v_chunk": vc, "S": plan.S,
+                   "parallelism": "single GPU"},
+        "forward_ms": round(ms_f, 4),
+        "gemm_TFLOP_per_s": round(gemm_flops / (ms / 1e3) / 1e12, 1),
+        "roofline": roof,
+        "memory": {"strip_bound_bytes": plan.strip_bound_bytes,
+                   "unchunked_logit_bytes": plan.unchunked_logit_bytes,
+                   "fwd_workspace_bytes": plan.fwd_workspace_bytes,
+                   "bwd_workspace_bytes": plan.bwd_workspace_bytes,
+                   "peak_alloc_during_steps": int(peak_extra)},
+        "stages": stages,
+        "wall_ms_per_step": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+
+        n_s = min(args.cpu_tokens, 512, N)
+        log(f"cpu baseline: fp64 oracle forward + backward of {n_s} tokens")
+        W64 = inp.to_f64(inp.W)
+        X64 = inp.to_f64(inp.X[:n_s])
+        c0 = time.perf_counter()
+        oracle.ce_forward_tokens(X64, W64, inp.targets[:n_s])
+        oracle.ce_backward_tokens(X64, W64, inp.targets[:n_s], inp.dloss[:n_s].astype(np.float64))
+        cpu_s = time.perf_counter() - c0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": round(n_s / cpu_s, 2), "unit": "tokens/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"first {n_s} of {N} tokens over the whole vocabulary: "
+                                         f"loss, dX and dW, {cpu_s:.1f} s"}
+        log(f"cpu baseline: {cpu_s:.2f} s, {threads} BLAS threads")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +286,8 @@ def main():
     if not torch.cuda.is_available():
         log("bench.py: no GPU visible")
         sys.exit(1)
+    if args.workload in datagen.CE_WORKLOADS:
+        return cce_main(args, datagen, np, torch, B)
     dev = torch.device("cuda:0")
     wl = datagen.WORKLOADS[args.workload]
     bf = wl.dtype == "bf16"

@@ -19,12 +19,14 @@ import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoebound.so")
-HEADER = os.path.join(os.path.dirname(PKG), "include", "moebound.h")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+HEADERS = (os.path.join(INCLUDE, "moebound.h"), os.path.join(INCLUDE, "cce.h"))
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 STAGES = {"router": 0, "topk": 1, "plan": 2, "gather": 3, "gemm_up": 4, "gemm_down": 5,
           "combine": 6}
 MOE_F32, MOE_BF16 = 0, 1
+CCE_STAGES = {"logits": 0, "fold": 1, "grad": 2, "dx": 3, "dw": 4}
 
 _c = ctypes
 _vp = _c.c_void_p
@@ -51,6 +53,15 @@ class MoeStats(_c.Structure):
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class CcePlan(_c.Structure):
+    _fields_ = [
+        ("magic", _c.c_uint32), ("dtype", _c.c_int32), ("N", _c.c_int64), ("V", _c.c_int64),
+        ("H", _c.c_int32), ("v_chunk", _c.c_int32), ("S", _c.c_int32), ("reserved0", _c.c_int32),
+        ("strip_bound_bytes", _c.c_int64), ("unchunked_logit_bytes", _c.c_int64),
+        ("fwd_workspace_bytes", _c.c_int64), ("bwd_workspace_bytes", _c.c_int64),
+    ]
 
 
 class MoeError(RuntimeError):
@@ -89,15 +100,27 @@ def lib() -> ctypes.CDLL:
     L.moe_debug_stage.restype = _c.c_int
     L.moe_debug_stage.argtypes = [_c.POINTER(MoePlan), _c.c_int32, _c.c_int32] + [_vp] * 9 + [
         _vp, _c.c_size_t, _vp]
+    L.cce_plan.restype = _c.c_int
+    L.cce_plan.argtypes = [_c.c_int64, _c.c_int32, _c.c_int64, _c.c_int32, _c.c_int32,
+                           _c.POINTER(CcePlan)]
+    L.cce_forward.restype = _c.c_int
+    L.cce_forward.argtypes = [_c.POINTER(CcePlan)] + [_vp] * 5 + [_vp, _c.c_size_t, _vp]
+    L.cce_backward.restype = _c.c_int
+    L.cce_backward.argtypes = [_c.POINTER(CcePlan)] + [_vp] * 7 + [_vp, _c.c_size_t, _vp]
+    L.cce_debug_stage.restype = _c.c_int
+    L.cce_debug_stage.argtypes = [_c.POINTER(CcePlan), _c.c_int32, _c.c_int32] + [_vp] * 8 + [
+        _vp, _c.c_size_t, _vp]
     _LIB = L
     return L
 
 
 def declared_functions() -> list:
-    """Function names declared in include/moebound.h."""
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    """Function names declared in include/moebound.h and include/cce.h."""
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:moe|cce)_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def status_string(status: int) -> str:
@@ -152,9 +175,10 @@ def moe_plan_chunks(N: int, H: int, F: int, E: int, k: int, c: int, K_max: int,
     return plan
 
 
-def workspace(plan: MoePlan, kind: str, device) -> torch.Tensor:
-    n = {"fwd": plan.fwd_workspace_bytes, "bwd": plan.bwd_workspace_bytes,
-         "debug": plan.debug_workspace_bytes}[kind]
+def workspace(plan, kind: str, device) -> torch.Tensor:
+    """Workspace of a MoePlan ("fwd", "bwd", "debug") or CcePlan ("fwd", "bwd")."""
+    n = getattr(plan, {"fwd": "fwd_workspace_bytes", "bwd": "bwd_workspace_bytes",
+                       "debug": "debug_workspace_bytes"}[kind])
     return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
 
 
@@ -268,3 +292,61 @@ def moe_debug_stage(plan: MoePlan, stage: str, chunk: int, X, W_r, router_bias, 
                                  _ptr(router_bias), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
                                  _ptr(Y), _ptr(topk_idx), _ptr(gates), _ptr(ws), ws.numel(),
                                  _stream(X.device, stream)), "moe_debug_stage")
+
+
+# ---- vocabulary projection with cross-entropy over vocabulary strips
+
+
+def cce_plan(N: int, H: int, V: int, v_chunk: int, dtype: int = MOE_BF16) -> CcePlan:
+    plan = CcePlan()
+    _check(lib().cce_plan(N, H, V, v_chunk, dtype, ctypes.byref(plan)), "cce_plan")
+    return plan
+
+
+def cce_forward(plan: CcePlan, X, W, targets, loss=None, lse=None, ws=None, stream=None):
+    """Returns (loss [N], lse [N]) fp32."""
+    dev = X.device
+    N, H, V = plan.N, plan.H, plan.V
+    _expect(X, "X", (N, H), torch.bfloat16, dev)
+    _expect(W, "W", (V, H), torch.bfloat16, dev)
+    _expect(targets, "targets", (N,), torch.int32, dev)
+    loss = torch.empty(N, dtype=torch.float32, device=dev) if loss is None else loss
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
+    _expect(loss, "loss", (N,), torch.float32, dev)
+    _expect(lse, "lse", (N,), torch.float32, dev)
+    ws = workspace(plan, "fwd", dev) if ws is None else ws
+    _check(lib().cce_forward(ctypes.byref(plan), _ptr(X), _ptr(W), _ptr(targets), _ptr(loss),
+                             _ptr(lse), _ptr(ws), ws.numel(), _stream(dev, stream)),
+           "cce_forward")
+    return loss, lse
+
+
+def cce_backward(plan: CcePlan, X, W, targets, lse, dloss, dX=None, dW=None, ws=None,
+                 stream=None):
+    """Returns (dX [N, H] bf16, dW [V, H] fp32)."""
+    dev = X.device
+    N, H, V = plan.N, plan.H, plan.V
+    f32 = torch.float32
+    for t, n, shp, d in ((X, "X", (N, H), torch.bfloat16), (W, "W", (V, H), torch.bfloat16),
+                         (targets, "targets", (N,), torch.int32), (lse, "lse", (N,), f32),
+                         (dloss, "dloss", (N,), f32)):
+        _expect(t, n, shp, d, dev)
+    dX = torch.empty((N, H), dtype=torch.bfloat16, device=dev) if dX is None else dX
+    dW = torch.empty((V, H), dtype=f32, device=dev) if dW is None else dW
+    _expect(dX, "dX", (N, H), torch.bfloat16, dev)
+    _expect(dW, "dW", (V, H), f32, dev)
+    ws = workspace(plan, "bwd", dev) if ws is None else ws
+    _check(lib().cce_backward(ctypes.byref(plan), _ptr(X), _ptr(W), _ptr(targets), _ptr(lse),
+                              _ptr(dloss), _ptr(dX), _ptr(dW), _ptr(ws), ws.numel(),
+                              _stream(dev, stream)), "cce_backward")
+    return dX, dW
+
+
+def cce_debug_stage(plan: CcePlan, stage: str, strip: int, X, W, targets, loss, lse, dloss, dX,
+                    dW, ws, stream=None):
+    """Re-launch one kernel of one strip (state from the last cce_forward or
+    cce_backward call on ``ws``)."""
+    _check(lib().cce_debug_stage(ctypes.byref(plan), CCE_STAGES[stage], strip, _ptr(X), _ptr(W),
+                                 _ptr(targets), _ptr(loss), _ptr(lse), _ptr(dloss), _ptr(dX),
+                                 _ptr(dW), _ptr(ws), ws.numel(), _stream(X.device, stream)),
+           "cce_debug_stage")

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoebound.so")
 
-SOURCES = ["api.hip", "route.hip", "plan.hip", "dispatch.hip", "gemm_fwd.hip", "gemm_bwd.hip"]
+SOURCES = ["api.hip", "route.hip", "plan.hip", "dispatch.hip", "gemm_fwd.hip", "gemm_bwd.hip",
+           "cce.hip", "gemm_cce.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

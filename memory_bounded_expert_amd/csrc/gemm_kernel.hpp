@@ -44,7 +44,9 @@ namespace moe {
 namespace gemm {
 
 enum class Mode { Rows, Dense, Expert };
-enum class Epi { Store, SwiGLU, SwiGLUSave, F32, BiasF32, AccF32 };
+// CEStats and CEGrad are the vocabulary-strip cross-entropy epilogues (LDS
+// pipeline, Dense mode only).
+enum class Epi { Store, SwiGLU, SwiGLUSave, F32, BiasF32, AccF32, CEStats, CEGrad };
 
 struct Params {
   const void* A;
@@ -63,7 +65,7 @@ struct Params {
   int ntiles;  // Rows mode: N-tiles per M-tile (N / BN)
   const int2* tiles;
   const int32_t* tile_count;
-  const int32_t* offsets;
+  const int32_t* offsets;  // Rows: expert row offsets; Expert: segment rows (or null: one of K)
   const float* bias;
   // Rows mode, LDS pipeline only: when set, row r of A is row
   // a_rows[r] / a_row_div of the matrix at A (a_src_rows rows): the permuted
@@ -74,6 +76,19 @@ struct Params {
   // Epi::AccF32, LDS pipeline only: store the tile (C = tile) instead of
   // accumulating; experts with no rows then store zeros.
   int acc_init;
+  // Epi::AccF32, LDS pipeline only (ignored with acc_init): load C into the
+  // accumulators before the K loop and store the result, so that C + A B is
+  // one fp32 accumulation chain continuing C's own.
+  int acc_chain;
+  // Epi::CEStats / Epi::CEGrad: the N columns of the tile grid are vocabulary
+  // entries ce_col0 + n; ce_targets[row] is the row's target entry.
+  const int32_t* ce_targets;
+  int64_t ce_col0;
+  float* ce_pmax;          // CEStats: [slice][M] max of a 1-wave column slice
+  float* ce_psum;          // CEStats: [slice][M] sum of exp(logit - that max)
+  float* ce_ytgt;          // CEStats: [M] the target's logit (its slice writes it)
+  const float* ce_lse;     // CEGrad: [M] log-normaliser
+  const float* ce_dl;      // CEGrad: [M] upstream gradient, 0 for ignored rows
 };
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }

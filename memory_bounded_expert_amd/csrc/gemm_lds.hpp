@@ -158,6 +158,27 @@ struct LdsCfg {
   static_assert(NS >= 3, "need at least three LDS stages");
 };
 
+// How an AccF32 kernel moves C: each wave carries its WM x WN block of C
+// through a private share of the (then idle) operand stages, SR rows at a
+// time, so that global memory sees 16-byte, row-contiguous accesses instead
+// of the fragments' 4-byte scatter.  Rows are padded by 4 floats so the four
+// row groups of a fragment land in distinct banks.
+template <class S, class C>
+struct AccGeom {
+  static constexpr int WM = S::BM / S::WGM, WN = S::BN / S::WGN;
+  static constexpr int LD = WN + 4;                        // padded row, floats
+  static constexpr int VW = WN / 4;                        // 16-byte vectors per row
+  static constexpr int PWB = C::NS * C::STAGE / C::WAVES;  // LDS bytes per wave
+  static constexpr int SR = acc_slice_rows<WM, LD, VW, PWB>();
+  static constexpr int NSL = WM / SR;                      // slices per operand group
+  static constexpr int NSUB = C::NB * NSL;
+  static constexpr int PER = SR * VW / 64;                 // vectors per lane per slice
+  static constexpr int FS = SR / 16;                       // fragment rows per slice
+  static_assert(SR % 16 == 0 && WM % SR == 0, "slices of whole fragment rows");
+  static_assert(SR * LD * 4 <= PWB, "accumulator slice must fit the wave's LDS share");
+  static_assert((SR * VW) % 64 == 0 && PER <= 8, "slice must split over the lanes");
+};
+
 // swizzle of a K-contiguous row of CK chunks (conflict-free ds_read_b128 of
 // 16 rows x one chunk)
 template <int CK>
@@ -214,8 +235,9 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
   } else {
     const ExpertTile t = expert_tile();
     e = t.e;
-    k_begin = p.offsets[e];
-    k_len = p.offsets[e + 1] - (int)k_begin;
+    // segment e's rows; without offsets, one segment of K rows
+    k_begin = p.offsets ? p.offsets[e] : 0;
+    k_len = p.offsets ? p.offsets[e + 1] - (int)k_begin : p.K;
     if (k_len <= 0 && !p.acc_init) return;  // nothing to add
     m0 = t.mt * BM;
     n0 = t.nt * BN;
@@ -271,7 +293,9 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
     rA2 = rA;
   }
   if constexpr (B_K) {
-    rB = make_srd(Bp + (int64_t)n0 * p.ldb, (int64_t)BN * p.ldb * TS);
+    // (Dense: B rows past N -- the ragged end of a vocabulary strip -- read as zeros)
+    const int64_t brows = MODE == Mode::Dense ? (int64_t)max(0, min(BN, p.N - n0)) : (int64_t)BN;
+    rB = make_srd(Bp + (int64_t)n0 * p.ldb, brows * p.ldb * TS);
     rB2 = KCAT ? make_srd(B2p + (int64_t)n0 * p.ldb, (int64_t)BN * p.ldb * TS) : rB;
   } else {
     const int64_t rows = (MODE == Mode::Expert) ? (int64_t)k_len : (int64_t)p.K;
@@ -350,6 +374,45 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[g][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  const int l16 = lane & 15, lg = lane >> 4;  // column/row within a fragment, k-group
+  if constexpr (EPI == Epi::AccF32) {
+    if (p.acc_chain && !p.acc_init) {
+      // C into the accumulators (rows past row_end as zeros), through this
+      // wave's LDS share, before the pipeline takes the stages over
+      using AG = AccGeom<S, C>;
+      float* stg = reinterpret_cast<float*>(smem + wave * AG::PWB);
+      const int rw0 = m0 + wm * WM, cw0 = n0 + wn * WN;
+#pragma unroll
+      for (int s = 0; s < AG::NSUB; ++s) {
+        const int g = s / AG::NSL, sl = s - g * AG::NSL;
+        const float* Cg = static_cast<const float*>(g == 0 ? p.C : p.C2) + (int64_t)e * p.c_estride;
+        f32x4_t v[AG::PER];
+#pragma unroll
+        for (int u = 0; u < AG::PER; ++u) {
+          const int idx = lane + u * 64, r = idx / AG::VW, c4 = idx - r * AG::VW;
+          const int row = rw0 + sl * AG::SR + r;
+          v[u] = row < row_end ? *reinterpret_cast<const f32x4_t*>(Cg + (int64_t)row * p.ldc + cw0 + c4 * 4)
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        wave_lds_sync();  // the previous slice's fragment reads are done
+#pragma unroll
+        for (int u = 0; u < AG::PER; ++u) {
+          const int idx = lane + u * 64, r = idx / AG::VW, c4 = idx - r * AG::VW;
+          *reinterpret_cast<f32x4_t*>(stg + r * AG::LD + c4 * 4) = v[u];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < AG::FS; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              acc[g][sl * AG::FS + i][j][q] = stg[(i * 16 + 4 * lg + q) * AG::LD + j * 16 + l16];
+      }
+      lds_barrier();  // every wave is done with its share before the stages refill
+    }
+  }
+
   // ---- MFMA operand reads.  Every fragment address is a lane-dependent base
   // plus a compile-time constant (stage, k-step, half, group and fragment
   // offsets), because each swizzle depends only on the lane:
@@ -362,7 +425,6 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
   //    + 4 rows for k-step and half.
   // The bases are re-laundered every K-step so that the compiler does not
   // hoist one address register per (stage, fragment) out of the loop.
-  const int l16 = lane & 15, lg = lane >> 4;  // column/row within a fragment, k-group
   const int trj = l16 >> 2, trq = l16 & 3;    // transposing read: row j, segment q
   constexpr int NBA = A_K ? KS : FM;
   constexpr int NBB = B_K ? KS : FN;
@@ -501,72 +563,114 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
   }
 
   if constexpr (EPI == Epi::AccF32) {
-    // Weight-gradient accumulation C += tile (fp32 read-modify-write).  Each
-    // wave moves its own WM x WN block through a private share of the free
-    // operand stages, SR rows at a time, so that HBM sees 16-byte,
-    // row-contiguous loads and stores instead of the fragments' 4-byte
-    // scatter.  The old values of slice s+1 are requested before slice s is
-    // added and stored, so the read latency overlaps the previous slice's
-    // work.  Each element is still old + new in one fp32 add (the product
-    // alone when acc_init).  The operand stages are free once every wave's
-    // last fragment reads are done (the barrier); after it each wave touches
-    // only its own share, so no further work-group barriers.  Rows are
-    // padded by 4 floats so the four row groups of a fragment land in
-    // distinct banks.
-    constexpr int LD = WN + 4;
-    constexpr int VW = WN / 4;                       // 16-byte vectors per wave row
-    constexpr int PWB = NS * C::STAGE / C::WAVES;    // LDS bytes per wave
-    constexpr int SR = acc_slice_rows<WM, LD, VW, PWB>();
-    constexpr int NSL = WM / SR;                     // slices per operand group
-    constexpr int NSUB = NB * NSL;
-    constexpr int PER = SR * VW / 64;                // vectors per lane per slice
-    constexpr int FS = SR / 16;                      // fragment rows per slice
-    static_assert(SR % 16 == 0 && WM % SR == 0, "slices of whole fragment rows");
-    static_assert(SR * LD * 4 <= PWB, "accumulator slice must fit the wave's LDS share");
-    static_assert((SR * VW) % 64 == 0 && PER <= 8, "slice must split over the lanes");
-    float* stg = reinterpret_cast<float*>(smem + wave * PWB);
+    // C += tile (fp32 read-modify-write), or C = tile with acc_init or
+    // acc_chain (the accumulators then already hold the whole sum).  Each
+    // wave moves its own block through its LDS share (AccGeom); the old
+    // values of slice s+1 are requested before slice s is added and stored,
+    // so the read latency overlaps the previous slice's work.  Each element
+    // is old + new in one fp32 add.  The operand stages are free once every
+    // wave's last fragment reads are done (the barrier); after it each wave
+    // touches only its own share.  Rows past row_end are neither read nor
+    // written.
+    using AG = AccGeom<S, C>;
+    float* stg = reinterpret_cast<float*>(smem + wave * AG::PWB);
     const int rw0 = m0 + wm * WM, cw0 = n0 + wn * WN;  // this wave's block
-    auto gptr = [&](int s, int u) __attribute__((always_inline)) {
-      const int g = s / NSL, sl = s - g * NSL;
-      const int idx = lane + u * 64, r = idx / VW, c4 = idx - r * VW;
-      float* Cg = static_cast<float*>(g == 0 ? p.C : p.C2) + (int64_t)e * p.c_estride;
-      return reinterpret_cast<f32x4_t*>(Cg + (int64_t)(rw0 + sl * SR + r) * p.ldc + cw0 + c4 * 4);
+    auto grow = [&](int s, int u) __attribute__((always_inline)) {
+      const int sl = s - (s / AG::NSL) * AG::NSL;
+      return rw0 + sl * AG::SR + (lane + u * 64) / AG::VW;
     };
-    const bool accumulate = !p.acc_init;
-    f32x4_t old[2][PER];
+    auto gptr = [&](int s, int u) __attribute__((always_inline)) {
+      const int g = s / AG::NSL;
+      const int idx = lane + u * 64, r = idx / AG::VW, c4 = idx - r * AG::VW;
+      float* Cg = static_cast<float*>(g == 0 ? p.C : p.C2) + (int64_t)e * p.c_estride;
+      return reinterpret_cast<f32x4_t*>(Cg + (int64_t)grow(s, u) * p.ldc + cw0 + c4 * 4);
+    };
+    const bool accumulate = !p.acc_init && !p.acc_chain;
+    f32x4_t old[2][AG::PER];
     if (accumulate) {
 #pragma unroll
-      for (int u = 0; u < PER; ++u) old[0][u] = *gptr(0, u);
+      for (int u = 0; u < AG::PER; ++u)
+        if (grow(0, u) < row_end) old[0][u] = *gptr(0, u);
     }
     lds_barrier();  // every wave's last fragment reads are done
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const int g = s / NSL, sl = s - g * NSL;
+    for (int s = 0; s < AG::NSUB; ++s) {
+      const int g = s / AG::NSL, sl = s - g * AG::NSL;
 #pragma unroll
-      for (int i = 0; i < FS; ++i)
+      for (int i = 0; i < AG::FS; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            stg[(i * 16 + 4 * lg + q) * LD + j * 16 + l16] = acc[g][sl * FS + i][j][q];
+            stg[(i * 16 + 4 * lg + q) * AG::LD + j * 16 + l16] = acc[g][sl * AG::FS + i][j][q];
       wave_lds_sync();
-      if (accumulate && s + 1 < NSUB) {
+      if (accumulate && s + 1 < AG::NSUB) {
 #pragma unroll
-        for (int u = 0; u < PER; ++u) old[(s + 1) & 1][u] = *gptr(s + 1, u);
+        for (int u = 0; u < AG::PER; ++u)
+          if (grow(s + 1, u) < row_end) old[(s + 1) & 1][u] = *gptr(s + 1, u);
       }
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int idx = lane + u * 64, r = idx / VW, c4 = idx - r * VW;
-        const f32x4_t add = *reinterpret_cast<const f32x4_t*>(stg + r * LD + c4 * 4);
-        *gptr(s, u) = accumulate ? old[s & 1][u] + add : add;
+      for (int u = 0; u < AG::PER; ++u) {
+        const int idx = lane + u * 64, r = idx / AG::VW, c4 = idx - r * AG::VW;
+        const f32x4_t add = *reinterpret_cast<const f32x4_t*>(stg + r * AG::LD + c4 * 4);
+        if (grow(s, u) < row_end) *gptr(s, u) = accumulate ? old[s & 1][u] + add : add;
       }
       wave_lds_sync();  // this slice's reads are done before the next slice's writes
     }
     return;
   }
 
-  if constexpr (MODE == Mode::Rows && (EPI == Epi::Store || EPI == Epi::SwiGLU ||
-                                      EPI == Epi::SwiGLUSave || EPI == Epi::F32)) {
+  if constexpr (EPI == Epi::CEStats) {
+    // Vocabulary-strip cross-entropy, forward: the tile's logits stay on
+    // chip.  Per row, each wave reduces its WN-column slice (columns past N,
+    // the ragged end of the strip, excluded) to the slice's max m and
+    // sum of exp(logit - m): first over the lane's own columns in column
+    // order, then over the 16 lanes of the row group by xor butterflies
+    // (commutative pairwise steps, so every lane ends with the same bits).
+    // Slice s of the strip covers columns [s WN, (s + 1) WN), the same
+    // vocabulary columns whatever the strip width.  The lane holding the
+    // row's target column also writes that logit.
+    const int col0 = n0 + wn * WN;
+    const int slice = col0 / WN;
+    const int64_t M = p.M;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = m0 + wm * WM + i * 16 + 4 * lg + q;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (col0 + j * 16 + l16 < p.N) mx = fmaxf(mx, acc[0][i][j][q]);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        float sm = 0.f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (col0 + j * 16 + l16 < p.N) sm += __expf(acc[0][i][j][q] - mx);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o);
+        if (row < row_end) {
+          if (l16 == 0) {
+            p.ce_pmax[slice * M + row] = mx;
+            p.ce_psum[slice * M + row] = sm;
+          }
+          const int64_t rel = (int64_t)p.ce_targets[row] - p.ce_col0 - col0;
+          if (rel >= 0 && rel < WN && (int)(rel & 15) == l16) {
+            float v = 0.f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              if ((int)(rel >> 4) == j) v = acc[0][i][j][q];
+            p.ce_ytgt[row] = v;
+          }
+        }
+      }
+    return;
+  }
+
+  if constexpr ((MODE == Mode::Rows && (EPI == Epi::Store || EPI == Epi::SwiGLU ||
+                                       EPI == Epi::SwiGLUSave || EPI == Epi::F32)) ||
+                (MODE == Mode::Dense && EPI == Epi::CEGrad)) {
     // Row-grouped outputs go out through LDS: each wave parks its fragment
     // values (computed exactly as below) in the free operand stages, slab by
     // slab of wave row slices, and the work-group then writes the slab with
@@ -610,6 +714,28 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
     };
     if constexpr (EPI == Epi::Store) {
       stage_store(static_cast<T*>(p.C), [&](int i, int j, int q) { return f2bf(acc[0][i][j][q]); });
+    } else if constexpr (EPI == Epi::CEGrad) {
+      // Vocabulary-strip cross-entropy, backward: the strip's logit gradient
+      // dl_row (exp(logit - lse_row) - [column == target_row]), bf16;
+      // columns past N (the ragged end of the strip) and rows with dl = 0
+      // (ignored tokens) store zeros.
+      float rlse[FM][4], rdl[FM][4];
+      int64_t rtc[FM][4];  // target column relative to this wave's first column
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = min(m0 + wm * WM + i * 16 + 4 * lg + q, row_end - 1);
+          rlse[i][q] = p.ce_lse[row];
+          rdl[i][q] = p.ce_dl[row];
+          rtc[i][q] = (int64_t)p.ce_targets[row] - p.ce_col0 - (n0 + wn * WN);
+        }
+      stage_store(static_cast<T*>(p.C), [&](int i, int j, int q) {
+        const int c = j * 16 + l16;
+        const float pr = __expf(acc[0][i][j][q] - rlse[i][q]);
+        const float gv = rdl[i][q] * (pr - (rtc[i][q] == c ? 1.f : 0.f));
+        return f2bf(n0 + wn * WN + c < p.N ? gv : 0.f);
+      });
     } else if constexpr (EPI == Epi::F32) {
       stage_store(static_cast<float*>(p.C), [&](int i, int j, int q) { return acc[0][i][j][q]; });
     } else {

@@ -183,4 +183,21 @@ hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bi
                        int64_t N, int H, int E, hipStream_t st, float* parts = nullptr,
                        int S = 1);
 
+// ---- vocabulary-strip cross-entropy (cce.hip, gemm_cce.hip)
+// Columns per statistics slice: one wave's columns of the logits tile.
+constexpr int kCceSlice = 128;
+// Logits of one strip, X [N][H] times Ws [w][H]^T.  grad = false: per-row
+// slice statistics into pmax/psum [slice][N] and the target logit into ytgt.
+// grad = true: the strip's logit gradient into G [N][ldg] bf16 (lse, dl [N]).
+hipError_t gemm_cce_logits(bool grad, const void* X, const void* Ws, int64_t N, int H, int w,
+                           int64_t col0, const int32_t* targets, float* pmax, float* psum,
+                           float* ytgt, const float* lse, const float* dl, void* G, int ldg,
+                           hipStream_t st);
+// dx [N][H] fp32 = (first ? 0 : dx) + G[:, :w] Ws, one accumulation chain.
+hipError_t gemm_cce_dx(const void* G, int ldg, const void* Ws, int64_t N, int H, int w,
+                       float* dx, bool first, hipStream_t st);
+// dws [w][H] fp32 = G[:, :w]^T X.
+hipError_t gemm_cce_dw(const void* G, int ldg, const void* X, int64_t N, int H, int w, float* dws,
+                       hipStream_t st);
+
 }  // namespace moe

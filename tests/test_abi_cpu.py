@@ -23,7 +23,8 @@ def test_exports_every_declared_function():
     names = B.declared_functions()
     assert set(names) == {"moe_plan_chunks", "moe_bounded_forward", "moe_bounded_backward",
                           "moe_status_string", "moe_debug_topk", "moe_debug_plan",
-                          "moe_debug_stage"}
+                          "moe_debug_stage", "cce_plan", "cce_forward", "cce_backward",
+                          "cce_debug_stage"}
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -38,11 +39,15 @@ def test_struct_layout_matches_c():
 #include <stdio.h>
 #include <stddef.h>
 #include "moebound.h"
+#include "cce.h"
 #define O(s, f) printf("%s.%s %zu\n", #s, #f, offsetof(s, f));
 int main(void) {
-  printf("plan %zu\nstats %zu\n", sizeof(moe_plan_t), sizeof(moe_stats_t));
+  printf("plan %zu\nstats %zu\ncce %zu\n", sizeof(moe_plan_t), sizeof(moe_stats_t),
+         sizeof(cce_plan_t));
   O(moe_plan_t, N) O(moe_plan_t, K) O(moe_plan_t, c_eff) O(moe_plan_t, debug_workspace_bytes)
   O(moe_stats_t, c_eff) O(moe_stats_t, workspace_bytes)
+  O(cce_plan_t, V) O(cce_plan_t, H) O(cce_plan_t, S) O(cce_plan_t, strip_bound_bytes)
+  O(cce_plan_t, bwd_workspace_bytes)
   return 0;
 }
 """
@@ -60,6 +65,9 @@ int main(void) {
         assert int(lines[f"moe_plan_t.{f}"]) == getattr(B.MoePlan, f).offset
     for f in ("c_eff", "workspace_bytes"):
         assert int(lines[f"moe_stats_t.{f}"]) == getattr(B.MoeStats, f).offset
+    assert int(lines["cce"]) == ctypes.sizeof(B.CcePlan)
+    for f in ("V", "H", "S", "strip_bound_bytes", "bwd_workspace_bytes"):
+        assert int(lines[f"cce_plan_t.{f}"]) == getattr(B.CcePlan, f).offset
 
 
 def test_plan_matches_oracle_exhaustively():
@@ -180,3 +188,64 @@ def test_bf16_forward_reads_permuted_inputs_in_place():
 def test_status_strings():
     for s in range(0, 6):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
+
+
+# ---- vocabulary-strip cross-entropy: plan and argument checks (host only)
+
+
+def test_cce_plan_strips_and_bounds():
+    for N, H, V, vc in ((8192, 7168, 200_000, 8192), (777, 512, 20_000, 4096), (1, 128, 1, 256),
+                        (5, 256, 300, 256), (3, 128, 1000, 1024)):
+        p = B.cce_plan(N, H, V, vc)
+        assert p.S == len(oracle.ce_strips(V, vc))
+        assert p.strip_bound_bytes == oracle.strip_bound_bytes(N, vc, V, 2)
+        assert p.unchunked_logit_bytes == N * V * 4
+        # forward workspace: one strip's slice statistics and the running
+        # state, O(N v_chunk / 128); backward: the bf16 strip and dX's fp32 sum
+        # (strip buffers are whole 256-column tiles wide)
+        cols = min(vc, -(-V // 256) * 256)
+        assert p.fwd_workspace_bytes <= 8 * N * cols // 128 + 3 * 4 * N + 5 * 256
+        assert p.bwd_workspace_bytes <= 2 * N * cols + 4 * N * H + 4 * N + 4 * 256
+        assert 2 * N * cols - p.strip_bound_bytes < 2 * N * 256
+    assert B.cce_plan(0, 128, 10, 256).S == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 128, 10, 256, 1), B.MOE_EINVAL),
+    ((4, 0, 10, 256, 1), B.MOE_EINVAL),
+    ((4, 128, 0, 256, 1), B.MOE_EINVAL),
+    ((4, 128, 10, 0, 1), B.MOE_EINVAL),
+    ((4, 128, 10, 256, 7), B.MOE_EINVAL),
+    ((4, 128, 10, 256, 0), B.MOE_EUNSUPPORTED),     # fp32
+    ((4, 192, 10, 256, 1), B.MOE_EUNSUPPORTED),     # H % 128
+    ((4, 128, 10, 384, 1), B.MOE_EUNSUPPORTED),     # v_chunk % 256
+    ((2**21, 512, 10, 256, 1), B.MOE_EUNSUPPORTED),  # N H >= 2^30
+    ((8, 128, 10, 2**23, 1), B.MOE_EUNSUPPORTED),   # v_chunk H >= 2^30
+])
+def test_cce_plan_errors(args, status):
+    plan = B.CcePlan()
+    assert B.lib().cce_plan(*args, ctypes.byref(plan)) == status
+
+
+def test_cce_argument_errors_before_any_launch():
+    L = B.lib()
+    p = B.cce_plan(300, 256, 5000, 1024)
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: every check below fails first
+    bad = B.CcePlan()
+    assert L.cce_forward(ctypes.byref(bad), *[fake] * 5, fake, 1 << 30, None) == B.MOE_EINVAL
+    assert L.cce_forward(ctypes.byref(p), None, *[fake] * 4, fake, 1 << 30, None) == B.MOE_EINVAL
+    assert L.cce_forward(ctypes.byref(p), *[fake] * 5, ctypes.c_void_p(0x100010), 1 << 30,
+                         None) == B.MOE_EINVAL
+    assert L.cce_forward(ctypes.byref(p), *[fake] * 5, fake, p.fwd_workspace_bytes - 1,
+                         None) == B.MOE_EWORKSPACE
+    assert L.cce_backward(ctypes.byref(p), *[fake] * 7, fake, p.bwd_workspace_bytes - 1,
+                          None) == B.MOE_EWORKSPACE
+    assert L.cce_backward(ctypes.byref(p), *[fake] * 6, None, fake, 1 << 30, None) == B.MOE_EINVAL
+    assert L.cce_debug_stage(ctypes.byref(p), 5, 0, *[fake] * 8, fake, 1 << 30, None) == B.MOE_EINVAL
+    assert L.cce_debug_stage(ctypes.byref(p), 0, p.S, *[fake] * 8, fake, 1 << 30, None) == B.MOE_EINVAL
+    assert L.cce_debug_stage(ctypes.byref(p), 3, 0, *[fake] * 8, fake, p.bwd_workspace_bytes - 1,
+                             None) == B.MOE_EWORKSPACE
+    # no tokens: forward is a no-op; backward still needs dW (it zeroes it)
+    p0 = B.cce_plan(0, 256, 5000, 1024)
+    assert L.cce_forward(ctypes.byref(p0), *[None] * 5, None, 0, None) == B.MOE_OK
+    assert L.cce_backward(ctypes.byref(p0), *[None] * 7, None, 0, None) == B.MOE_EINVAL
