@@ -60,6 +60,9 @@ hipError_t gemm_cce_dw(const void* G, int ldg, const void* X, int64_t N, int H, 
   p.C = dws; p.ldc = H; p.c_estride = 0;
   p.M = w; p.N = H; p.K = (int)N;  // one segment: rows [0, N) of G and X (no offsets)
   p.acc_init = 1;
+  // K = N rows is long: 8 x 8 blocks of tiles run together and share their
+  // K-tiles through L2 (the N-tile-fastest order re-reads all of X per M-tile)
+  p.tile_group = kCceDwGroup;
   const int bn = H % 256 == 0 ? 256 : 128;
   const dim3 grid((unsigned)ceil_div(w, 128), (unsigned)(H / bn), 1u);
   if (bn == 256)

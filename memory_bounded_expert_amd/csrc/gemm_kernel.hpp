@@ -63,6 +63,7 @@ struct Params {
   int64_t c_estride;  // elements between experts' C (Expert mode)
   int M, N, K, Kseg;
   int ntiles;  // Rows mode: N-tiles per M-tile (N / BN)
+  int tile_group;  // Expert mode: M-tiles per dispatch group (0 or 1: N-tile fastest)
   const int2* tiles;
   const int32_t* tile_count;
   const int32_t* offsets;  // Rows: expert row offsets; Expert: segment rows (or null: one of K)
@@ -168,20 +169,33 @@ __device__ __forceinline__ int xcd_contiguous(int L, int total) {
 
 // Weight-gradient grids are (M-tiles, N-tiles, experts).  The tiles of one
 // expert all read that expert's activation rows, so they go to one XCD (the
-// renumbered ids run expert by expert, N-tile fastest) and the rows are
-// fetched into one L2 instead of eight.
+// renumbered ids run expert by expert) and the rows are fetched into one L2
+// instead of eight.  Inside an expert the ids run N-tile fastest, or, with
+// group > 1, in groups of `group` M-tiles (the last may be short) with the
+// M-tile fastest inside a group: then the work-groups an XCD runs together
+// form a group x (their number / group) block of tiles that shares its
+// A and B K-tiles through L2 -- what a long K (many rows) needs.
 struct ExpertTile {
   int e, mt, nt;
 };
-__device__ __forceinline__ ExpertTile expert_tile() {
+__device__ __forceinline__ ExpertTile expert_tile(int group) {
   const int gx = gridDim.x, gy = gridDim.y, per = gx * gy;
   const int L = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
   const int lid = xcd_contiguous(L, per * gridDim.z);
   ExpertTile t;
   t.e = lid / per;
   const int rem = lid - t.e * per;
-  t.mt = rem / gy;
-  t.nt = rem - t.mt * gy;
+  if (group > 1) {
+    const int span = group * gy;
+    const int grp = rem / span;
+    const int gsz = min(group, gx - grp * group);
+    const int r = rem - grp * span;
+    t.nt = r / gsz;
+    t.mt = grp * group + (r - t.nt * gsz);
+  } else {
+    t.mt = rem / gy;
+    t.nt = rem - t.mt * gy;
+  }
   return t;
 }
 
@@ -238,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
     m0 = blockIdx.x * BM;
     row_end = p.M;
   } else {
-    const ExpertTile t = expert_tile();
+    const ExpertTile t = expert_tile(p.tile_group);
     e = t.e;
     k_begin = p.offsets[e];
     k_len = p.offsets[e + 1] - (int)k_begin;

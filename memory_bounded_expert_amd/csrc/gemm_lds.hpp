@@ -233,7 +233,7 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
     row_end = p.M;
     if (gridDim.z > 1) k_len = p.Kseg;
   } else {
-    const ExpertTile t = expert_tile();
+    const ExpertTile t = expert_tile(p.tile_group);
     e = t.e;
     // segment e's rows; without offsets, one segment of K rows
     k_begin = p.offsets ? p.offsets[e] : 0;

@@ -186,6 +186,8 @@ hipError_t gemm_router(int dtype, const void* X, const void* Wr, const float* bi
 // ---- vocabulary-strip cross-entropy (cce.hip, gemm_cce.hip)
 // Columns per statistics slice: one wave's columns of the logits tile.
 constexpr int kCceSlice = 128;
+// M-tiles per dispatch group of the weight-gradient product (expert_tile).
+constexpr int kCceDwGroup = 8;
 // Logits of one strip, X [N][H] times Ws [w][H]^T.  grad = false: per-row
 // slice statistics into pmax/psum [slice][N] and the target logit into ytgt.
 // grad = true: the strip's logit gradient into G [N][ldg] bf16 (lse, dl [N]).
