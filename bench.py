@@ -247,7 +247,7 @@ def cce_main(args, datagen, np, torch, B):
         import oracle
         from threadpoolctl import threadpool_info
 
-        n_s = min(args.cpu_tokens, 512, N)
+        n_s = min(args.cpu_tokens, 1536, N)
         log(f"cpu baseline: fp64 oracle forward + backward of {n_s} tokens")
         W64 = inp.to_f64(inp.W)
         X64 = inp.to_f64(inp.X[:n_s])

@@ -71,24 +71,37 @@ CceLayout cce_layout(int64_t N, int H, int cols, bool backward) {
 // running state of the earlier strips (first: start from the empty state;
 // last: finish with lse = m + log z and the loss).  An empty slice (every
 // column past the vocabulary end) has max -inf and is skipped.
-__global__ __launch_bounds__(kCceThreads) void cce_fold_kernel(
+// One thread per token, 64-token blocks (a batch of a few thousand tokens
+// still spreads over the CUs); the slice pairs are loaded kFoldBatch at a time
+// ahead of the sequential fold so their latency overlaps.
+constexpr int kFoldThreads = 64;
+constexpr int kFoldBatch = 8;
+__global__ __launch_bounds__(kFoldThreads) void cce_fold_kernel(
     const float* __restrict__ pmax, const float* __restrict__ psum, int nslices, int64_t N,
     float* __restrict__ m, float* __restrict__ z, int first, int last,
     const float* __restrict__ ytgt, const int32_t* __restrict__ targets, int64_t V,
     float* __restrict__ loss, float* __restrict__ lse) {
-  const int64_t t = (int64_t)blockIdx.x * kCceThreads + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * kFoldThreads + threadIdx.x;
   if (t >= N) return;
   float mm = first ? -INFINITY : m[t];
   float zz = first ? 0.f : z[t];
-  for (int s = 0; s < nslices; ++s) {
-    const float a = pmax[(int64_t)s * N + t];
-    if (a == -INFINITY) continue;
-    const float b = psum[(int64_t)s * N + t];
-    if (a > mm) {
-      zz = zz * expf(mm - a) + b;  // m' = a: the old normaliser is rescaled
-      mm = a;
-    } else {
-      zz = zz + b * expf(a - mm);  // m' = m: the slice's sum is rescaled
+  for (int s0 = 0; s0 < nslices; s0 += kFoldBatch) {
+    float a[kFoldBatch], b[kFoldBatch];
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      const bool in = s0 + u < nslices;
+      a[u] = in ? pmax[(int64_t)(s0 + u) * N + t] : -INFINITY;
+      b[u] = in ? psum[(int64_t)(s0 + u) * N + t] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      if (a[u] == -INFINITY) continue;  // empty slice (or past the strip's last)
+      if (a[u] > mm) {
+        zz = zz * expf(mm - a[u]) + b[u];  // m' = a: the old normaliser is rescaled
+        mm = a[u];
+      } else {
+        zz = zz + b[u] * expf(a[u] - mm);  // m' = m: the slice's sum is rescaled
+      }
     }
   }
   if (last) {
@@ -191,8 +204,8 @@ MOE_API int cce_forward(const cce_plan_t* plan, const void* X, const void* W,
                               nullptr, nullptr, 0, st));
     // slices the GEMM wrote: whole 256-column tiles, two slices each
     const int nsl = (int)ceil_div(w, 256) * (256 / kCceSlice);
-    cce_fold_kernel<<<blocks(P.N), kCceThreads, 0, st>>>(pmax, psum, nsl, P.N, m, z, s == 0,
-                                                      s == P.S - 1, ytgt, targets, P.V, loss, lse);
+    cce_fold_kernel<<<(unsigned)ceil_div(P.N, kFoldThreads), kFoldThreads, 0, st>>>(
+        pmax, psum, nsl, P.N, m, z, s == 0, s == P.S - 1, ytgt, targets, P.V, loss, lse);
     CCE_CHECK(hipGetLastError());
   }
   return MOE_OK;
@@ -268,7 +281,7 @@ MOE_API int cce_debug_stage(const cce_plan_t* plan, int32_t stage, int32_t strip
       break;
     case CCE_STAGE_FOLD: {
       const int nsl = (int)ceil_div(w, 256) * (256 / kCceSlice);
-      cce_fold_kernel<<<blocks(P.N), kCceThreads, 0, st>>>(
+      cce_fold_kernel<<<(unsigned)ceil_div(P.N, kFoldThreads), kFoldThreads, 0, st>>>(
           (float*)(ws + L.pmax), (float*)(ws + L.psum), nsl, P.N, (float*)(ws + L.m),
           (float*)(ws + L.z), strip == 0, strip == P.S - 1, (float*)(ws + L.ytgt), targets, P.V,
           loss, lse);
