@@ -54,7 +54,12 @@ Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_d
     if (pass == Pass::Backward) {
       L.a = take(rows * F * b);
       L.u = take(rows * F * b);
-      L.dh = take(rows * F * 4);
+      // fp32: dY W_down^T for the separate SwiGLU backward; bf16: the dh
+      // GEMM's per-N-tile dgate shares (at most F/64 tiles)
+      if (p.dtype == MOE_BF16)
+        L.dgp = take(((size_t)F / 64) * rows * 4);
+      else
+        L.dh = take(rows * F * 4);
       L.wrt = take(E * H * b);
       if (need_dgates) L.dgates = take(N * k * 4);
     }
@@ -261,6 +266,8 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
   void* a = ws + L.a;  // a, then da
   void* u = ws + L.u;  // u, then du
   float* dh = (float*)(ws + L.dh);
+  float* dgp = (float*)(ws + L.dgp);
+  const bool fused_swiglu = P.dtype == MOE_BF16;
   for (int i = 0; i < P.K; ++i) {
     const ChunkGeom g = chunk_geom(P.N, P.K, P.k, i);
     const int64_t R = (int64_t)P.k * g.n;
@@ -271,19 +278,25 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
     MOE_CHECK(gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, a, u, P.H, P.F, st));
     // backward through the chunk
     MOE_CHECK(launch_gather(P.dtype, dY, o, perm_i, R, P.k, P.N, P.H, st));
-    MOE_CHECK(gemm_dh(P.dtype, rg, o, W_down, dh, P.H, P.F, st));
-    MOE_CHECK(launch_swiglu_bwd(P.dtype, dh, a, u, h, perm_i, gates, dg, R, P.F, P.N * P.k, st));
+    if (fused_swiglu) {
+      MOE_CHECK(gemm_dh_swiglu(rg, o, W_down, a, u, h, perm_i, gates, dgp, (int64_t)P.k * P.c_eff,
+                               P.N * P.k, P.H, P.F, st));
+    } else {
+      MOE_CHECK(gemm_dh(P.dtype, rg, o, W_down, dh, P.H, P.F, st));
+      MOE_CHECK(launch_swiglu_bwd(P.dtype, dh, a, u, h, perm_i, gates, dg, R, P.F, P.N * P.k, st));
+    }
     MOE_CHECK(gemm_wgrad_d(P.dtype, rg.offsets, h, o, dW_down, P.E, P.H, P.F, st, wg_init && i == 0));
     MOE_CHECK(gemm_wgrad_gu(P.dtype, rg.offsets, xp, a, u, dW_gate, dW_up, P.E, P.H, P.F, st,
                             wg_init && i == 0));
     MOE_CHECK(gemm_dx(P.dtype, rg, a, u, W_gate, W_up, o, P.H, P.F, st));
     MOE_CHECK(launch_combine_bwd(P.dtype, o, wrt, topk_idx, pb.pos, gates, dg, dX, dlogits, P.N,
-                                 P.K, i, g.n, P.k, P.E, P.H, st));
+                                 P.K, i, g.n, P.k, P.E, P.H, st, fused_swiglu ? dgp : nullptr,
+                                 fused_swiglu ? dh_ntiles(rg, P.F) : 0, (int64_t)P.k * P.c_eff));
     if (dW_r)
       MOE_CHECK(launch_dwr(P.dtype, xp, perm_i, rg.offsets, dlogits, dW_r, P.k, P.E, P.H, P.N, st));
   }
   fill_stats(stats, P, launches, L.total,
-             (size_t)P.k * P.c_eff * P.F * (3 * elem_bytes(P.dtype) + 4));
+             (size_t)P.k * P.c_eff * P.F * (3 * elem_bytes(P.dtype) + (fused_swiglu ? 0 : 4)));
   return MOE_OK;
 }
 

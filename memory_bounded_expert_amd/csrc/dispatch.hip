@@ -175,25 +175,43 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(
 //   experts and 0 elsewhere,
 //   dX[t] = sum_s dXp[pos[t,s]] + sum_s dl_s W_r^T[S_t[s]]  (fp32, slot order,
 //   one rounding).
+// With dgp set, slot s's dgate is first summed over the nparts shares
+// dgp[nt][pos[t,s]] (nt ascending) and stored to dgates.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
     const T* __restrict__ dXp, const T* __restrict__ WrT, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ pos, const float* __restrict__ gates,
-    const float* __restrict__ dgates, T* __restrict__ dX, float* __restrict__ dlogits, int K,
-    int i, int64_t n_i, int k, int E, int H) {
+    float* __restrict__ dgates, T* __restrict__ dX, float* __restrict__ dlogits, int K,
+    int i, int64_t n_i, int k, int E, int H, const float* __restrict__ dgp, int nparts,
+    int64_t prow) {
   constexpr int EPC = Elem<T>::kPer16B;
   __shared__ float dl[64];
+  __shared__ float dgs[64];
   __shared__ int ex[64];
   __shared__ int64_t rows[64];
   const int cpr = H / EPC;
   for (int64_t j = blockIdx.x; j < n_i; j += gridDim.x) {
     const int64_t t = i + j * (int64_t)K;
+    if ((int)threadIdx.x < k) {
+      const int s = threadIdx.x;
+      float v;
+      if (dgp) {
+        const int64_t r = pos[t * k + s];
+        v = 0.f;
+        for (int nt = 0; nt < nparts; ++nt) v += dgp[nt * prow + r];
+        dgates[t * k + s] = v;
+      } else {
+        v = dgates[t * k + s];
+      }
+      dgs[s] = v;
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
       float sdot = 0.f;
-      for (int s = 0; s < k; ++s) sdot = fmaf(gates[t * k + s], dgates[t * k + s], sdot);
+      for (int s = 0; s < k; ++s) sdot = fmaf(gates[t * k + s], dgs[s], sdot);
       for (int s = 0; s < k; ++s) {
         const float g = gates[t * k + s];
-        dl[s] = g * (dgates[t * k + s] - sdot);
+        dl[s] = g * (dgs[s] - sdot);
         int e = idx[t * k + s];
         ex[s] = ((unsigned)e < (unsigned)E) ? e : 0;
         rows[s] = pos[t * k + s];
@@ -356,20 +374,21 @@ hipError_t launch_swiglu_bwd(int dtype, const float* dh, void* a_da, void* u_du,
 }
 
 hipError_t launch_combine_bwd(int dtype, const void* dXp, const void* WrT, const int32_t* idx,
-                              const int32_t* pos, const float* gates, const float* dgates,
+                              const int32_t* pos, const float* gates, float* dgates,
                               void* dX, float* dlogits, int64_t N, int K, int i, int64_t n_i,
-                              int k, int E, int H, hipStream_t st) {
+                              int k, int E, int H, hipStream_t st, const float* dgp, int nparts,
+                              int64_t prow) {
   (void)N;
   if (n_i == 0) return hipSuccess;
   const unsigned grid = grid_for(n_i, 1);
   if (dtype == MOE_BF16)
     combine_bwd_kernel<bf16_t><<<grid, kThreads, 0, st>>>(
         (const bf16_t*)dXp, (const bf16_t*)WrT, idx, pos, gates, dgates, (bf16_t*)dX, dlogits, K,
-        i, n_i, k, E, H);
+        i, n_i, k, E, H, dgp, nparts, prow);
   else
     combine_bwd_kernel<float><<<grid, kThreads, 0, st>>>((const float*)dXp, (const float*)WrT, idx,
                                                          pos, gates, dgates, (float*)dX, dlogits, K,
-                                                         i, n_i, k, E, H);
+                                                         i, n_i, k, E, H, dgp, nparts, prow);
   return hipGetLastError();
 }
 

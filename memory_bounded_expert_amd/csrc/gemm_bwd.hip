@@ -22,6 +22,18 @@ hipError_t dh_bf16(const Params& p, dim3 grid, int bn, int rt, hipStream_t st) {
   return launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, false, true, true, false, Epi::F32>(p, grid, st);
 }
 
+hipError_t dh_swiglu_bf16(const Params& p, dim3 grid, int bn, int rt, hipStream_t st) {
+  constexpr Epi E = Epi::SwiGLUBwd;
+  if (rt == kRowTileLarge) {
+    if (bn == 256) return launch_lds<Mode::Rows, Big<256>, false, true, true, false, E>(p, grid, st);
+    if (bn == 128) return launch_lds<Mode::Rows, Big<128>, false, true, true, false, E>(p, grid, st);
+    return hipErrorInvalidValue;
+  }
+  if (bn == 256) return launch_lds<Mode::Rows, Shape<128, 256, 2, 4, 64, 1>, false, true, true, false, E>(p, grid, st);
+  if (bn == 128) return launch_lds<Mode::Rows, Shape<128, 128, 2, 4, 64, 1>, false, true, true, false, E>(p, grid, st);
+  return launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, false, true, true, false, E>(p, grid, st);
+}
+
 hipError_t dx_bf16(const Params& p, dim3 grid, int bn, int rt, hipStream_t st) {
   if (rt == kRowTileLarge) {
     if (bn == 256) return launch_lds<Mode::Rows, Big<256>, false, true, true, true, Epi::Store>(p, grid, st);
@@ -87,6 +99,27 @@ hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd
   p.ntiles = F / bn;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
   return dtype == MOE_BF16 ? dh_bf16(p, grid, bn, g.row_tile, st) : dh_t<float>(p, grid, bn, st);
+}
+
+int dh_ntiles(const RowsGeom& g, int F) {
+  return F / (g.row_tile == kRowTileLarge ? (F % 256 == 0 ? 256 : 128) : pick_bn(F, true));
+}
+
+hipError_t gemm_dh_swiglu(const RowsGeom& g, const void* dYp, const void* Wd, void* a_da,
+                          void* u_du, void* h_hg, const int32_t* perm, const float* gates,
+                          float* dgp, int64_t rows, int64_t Nk, int H, int F, hipStream_t st) {
+  if (g.grid_m == 0) return hipSuccess;
+  Params p{};
+  p.A = dYp; p.lda = H;
+  p.B = Wd; p.ldb = H; p.b_estride = (int64_t)F * H;  // row f of W_down[e] holds K = H
+  p.C = h_hg; p.C2 = a_da; p.C3 = u_du; p.ldc = F;
+  p.N = F; p.K = H;
+  p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
+  p.sw_perm = perm; p.sw_gates = gates; p.sw_dgp = dgp; p.sw_rows = rows; p.sw_nk = Nk;
+  p.ntiles = dh_ntiles(g, F);
+  const int bn = F / p.ntiles;
+  const dim3 grid((unsigned)(g.grid_m * p.ntiles));
+  return dh_swiglu_bf16(p, grid, bn, g.row_tile, st);
 }
 
 hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du, const void* Wg,

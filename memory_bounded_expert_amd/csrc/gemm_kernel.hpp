@@ -46,7 +46,9 @@ namespace gemm {
 enum class Mode { Rows, Dense, Expert };
 // CEStats and CEGrad are the vocabulary-strip cross-entropy epilogues (LDS
 // pipeline, Dense mode only).
-enum class Epi { Store, SwiGLU, SwiGLUSave, F32, BiasF32, AccF32, CEStats, CEGrad };
+// SwiGLUBwd is the SwiGLU backward fused into dY W_down^T (LDS pipeline,
+// Rows mode only).
+enum class Epi { Store, SwiGLU, SwiGLUSave, F32, BiasF32, AccF32, CEStats, CEGrad, SwiGLUBwd };
 
 struct Params {
   const void* A;
@@ -90,6 +92,14 @@ struct Params {
   float* ce_ytgt;          // CEStats: [M] the target's logit (its slice writes it)
   const float* ce_lse;     // CEGrad: [M] log-normaliser
   const float* ce_dl;      // CEGrad: [M] upstream gradient, 0 for ignored rows
+  // Epi::SwiGLUBwd: C = h (then g h), C2 = a (then da), C3 = u (then du),
+  // row r's pair sw_perm[r] (< sw_nk) and its gate; sw_dgp[n-tile][row]
+  // (row stride sw_rows) receives the tile's share of sum_f dh' h.
+  const int32_t* sw_perm;
+  const float* sw_gates;
+  float* sw_dgp;
+  int64_t sw_rows;
+  int64_t sw_nk;
 };
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }

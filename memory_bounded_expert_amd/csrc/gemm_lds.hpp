@@ -668,6 +668,87 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
     return;
   }
 
+  if constexpr (MODE == Mode::Rows && EPI == Epi::SwiGLUBwd) {
+    // SwiGLU backward fused into dh' = dYp W_down^T, which is never stored.
+    // Per row r (pair p = sw_perm[r], gate g) and column f, with s =
+    // sigmoid(a): da = g dh' u s (1 + a (1 - s)), du = g dh' a s, hg = g h,
+    // written over a, u and h; and the tile's share of dgate_p = sum_f dh' h,
+    // written to sw_dgp[n-tile][r] (the tiles are added in order later).
+    // dh' goes through the free operand stages slab by slab (as the staged
+    // stores), so each thread takes 8 consecutive columns of one row: 16-byte
+    // accesses to a, u and h, and the row's share is a lane-order sum then an
+    // xor butterfly over the G8 threads of the row (consecutive lanes).
+    constexpr int LD = BN + 4;  // padded row, floats
+    constexpr int G8 = BN / 8;  // 8-column groups per row
+    constexpr int SLAB_FIT = (NS * C::STAGE) / (WM * LD * 4);
+    constexpr int SLAB = SLAB_FIT >= S::WGM ? S::WGM : (SLAB_FIT >= 2 && S::WGM % 2 == 0 ? 2 : 1);
+    constexpr int SR = SLAB * WM;
+    static_assert(SR * LD * 4 <= NS * C::STAGE, "staging must fit the LDS stages");
+    static_assert(S::WGM % SLAB == 0, "slabs of whole wave row slices");
+    static_assert(64 % G8 == 0 && (SR * G8) % C::THREADS == 0,
+                  "a row's threads share one wave; every thread runs the same iterations");
+    float* stg = reinterpret_cast<float*>(smem);
+    T* Ch = static_cast<T*>(p.C);
+    T* Ca = static_cast<T*>(p.C2);
+    T* Cu = static_cast<T*>(p.C3);
+    float* dgp = p.sw_dgp + (int64_t)(n0 / BN) * p.sw_rows;
+#pragma unroll
+    for (int sl = 0; sl < S::WGM / SLAB; ++sl) {
+      lds_barrier();  // previous users of the LDS are done
+      if (wm / SLAB == sl) {
+        const int r0 = (wm - sl * SLAB) * WM;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              stg[(r0 + i * 16 + 4 * lg + q) * LD + wn * WN + j * 16 + l16] = acc[0][i][j][q];
+      }
+      lds_barrier();
+      const int row0 = m0 + sl * SR;
+      for (int idx = tid; idx < SR * G8; idx += C::THREADS) {
+        const int r = idx / G8, c = idx - r * G8;
+        const int grow = row0 + r;
+        const bool ok = grow < row_end;
+        float part = 0.f;
+        if (ok) {
+          float dv[8], av[8], uv[8], hv[8];
+          const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(stg + r * LD + c * 8);
+          const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(stg + r * LD + c * 8 + 4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            dv[q] = d0[q];
+            dv[q + 4] = d1[q];
+          }
+          const int32_t pr = p.sw_perm[grow];
+          const float g = (uint64_t)pr < (uint64_t)p.sw_nk ? p.sw_gates[pr] : 0.f;
+          const int64_t o = (int64_t)grow * p.ldc + n0 + c * 8;
+          unpack16(*reinterpret_cast<const u32x4_t*>(Ca + o), av, T());
+          unpack16(*reinterpret_cast<const u32x4_t*>(Cu + o), uv, T());
+          unpack16(*reinterpret_cast<const u32x4_t*>(Ch + o), hv, T());
+          float da[8], du[8], hg[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            part = fmaf(dv[q], hv[q], part);
+            const float sa = 1.f / (1.f + expf(-av[q]));
+            const float d = g * dv[q];
+            da[q] = d * uv[q] * sa * (1.f + av[q] * (1.f - sa));
+            du[q] = d * av[q] * sa;
+            hg[q] = g * hv[q];
+          }
+          *reinterpret_cast<u32x4_t*>(Ca + o) = pack16(da, T());
+          *reinterpret_cast<u32x4_t*>(Cu + o) = pack16(du, T());
+          *reinterpret_cast<u32x4_t*>(Ch + o) = pack16(hg, T());
+        }
+#pragma unroll
+        for (int m = 1; m < G8; m <<= 1) part += __shfl_xor(part, m);
+        if (ok && c == 0) dgp[grow] = part;
+      }
+    }
+    return;
+  }
+
   if constexpr ((MODE == Mode::Rows && (EPI == Epi::Store || EPI == Epi::SwiGLU ||
                                        EPI == Epi::SwiGLUSave || EPI == Epi::F32)) ||
                 (MODE == Mode::Dense && EPI == Epi::CEGrad)) {

@@ -90,7 +90,8 @@ struct Layout {
   size_t h = 0;           // [k c_eff][F]  h (forward); h, then g*h (backward)
   size_t a = 0;           // [k c_eff][F]  backward: a, then da
   size_t u = 0;           // [k c_eff][F]  backward: u, then du
-  size_t dh = 0;          // [k c_eff][F] f32 backward: dY W_down^T
+  size_t dh = 0;          // [k c_eff][F] f32 backward, fp32: dY W_down^T
+  size_t dgp = 0;         // [F/64][k c_eff] f32 backward, bf16: dgate shares per N-tile
   size_t wrt = 0;         // [E][H] backward: W_r transposed
   size_t dgates = 0;      // [N*k] f32 backward, when the caller passes none
   size_t total = 0;
@@ -137,10 +138,13 @@ hipError_t launch_transpose(int dtype, const void* src, void* dst, int rows, int
 hipError_t launch_swiglu_bwd(int dtype, const float* dh, void* a_da, void* u_du, void* h_hg,
                              const int32_t* perm_chunk, const float* gates, float* dgates,
                              int64_t R, int F, int64_t Nk, hipStream_t st);
+// With dgp != nullptr the slots' dgates are first summed from the dh GEMM's
+// per-N-tile shares (dgp [nparts][prow], tiles in order) and written to dgates.
 hipError_t launch_combine_bwd(int dtype, const void* dXp, const void* WrT, const int32_t* idx,
-                              const int32_t* pos, const float* gates, const float* dgates,
+                              const int32_t* pos, const float* gates, float* dgates,
                               void* dX, float* dlogits, int64_t N, int K, int i, int64_t n_i,
-                              int k, int E, int H, hipStream_t st);
+                              int k, int E, int H, hipStream_t st, const float* dgp = nullptr,
+                              int nparts = 0, int64_t prow = 0);
 hipError_t launch_dwr(int dtype, const void* Xp, const int32_t* perm_chunk, const int32_t* offsets,
                       const float* dlogits, float* dWr, int k, int E, int H, int64_t N,
                       hipStream_t st);
@@ -165,6 +169,13 @@ hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd
 // dh = dYp W_down[e]^T (fp32 out)
 hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd, float* dh, int H,
                    int F, hipStream_t st);
+// bf16: dh' = dYp W_down[e]^T with the SwiGLU backward in the epilogue (as
+// launch_swiglu_bwd, dh' never stored): da, du, g h over a, u, h; the per
+// N-tile shares of dgate into dgp [dh_ntiles][rows].
+int dh_ntiles(const RowsGeom& g, int F);
+hipError_t gemm_dh_swiglu(const RowsGeom& g, const void* dYp, const void* Wd, void* a_da,
+                          void* u_du, void* h_hg, const int32_t* perm, const float* gates,
+                          float* dgp, int64_t rows, int64_t Nk, int H, int F, hipStream_t st);
 // dXp = da W_gate[e]^T + du W_up[e]^T
 hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du, const void* Wg,
                    const void* Wu, void* dXp, int H, int F, hipStream_t st);
