@@ -43,6 +43,13 @@ Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_d
   L.offsets = take(K * (E + 1) * 4);
   L.tiles = take(K * (size_t)L.max_tiles * 8);
   L.tile_count = take(K * 4);
+  if (pass == Pass::Forward && split_tiles(p)) {
+    L.split = true;
+    L.small_tiles = take(K * E * 8);
+    L.small_count = take(K * 4);
+    L.long_tiles = take(K * (size_t)L.max_tiles * 8);
+    L.long_count = take(K * 4);
+  }
   if (pass != Pass::Debug) {
     L.perm = take(N * k * 4);
     L.pos = take(N * k * 4);
@@ -85,6 +92,10 @@ PlanBuffers plan_buffers(char* ws, const Layout& L, int32_t* offsets, int32_t* p
   b.nblk = L.nblk;
   b.max_tiles = L.max_tiles;
   b.row_tile = L.row_tile;
+  b.small_tiles = L.split ? (int2*)(ws + L.small_tiles) : nullptr;
+  b.small_count = L.split ? (int32_t*)(ws + L.small_count) : nullptr;
+  b.long_tiles = L.split ? (int2*)(ws + L.long_tiles) : nullptr;
+  b.long_count = L.split ? (int32_t*)(ws + L.long_count) : nullptr;
   return b;
 }
 
@@ -95,6 +106,25 @@ RowsGeom rows_geom(const PlanBuffers& b, const moe_plan_t& P, int i, int64_t R) 
   g.offsets = b.offsets + (int64_t)i * (P.E + 1);
   g.grid_m = max_row_tiles(R, P.E, b.row_tile);
   g.row_tile = b.row_tile;
+  return g;
+}
+
+// The long segments' list of a split plan (row_tile-row tiles).
+RowsGeom long_geom(const PlanBuffers& b, const moe_plan_t& P, int i, int64_t R) {
+  RowsGeom g = rows_geom(b, P, i, R);
+  g.tiles = b.long_tiles + (int64_t)i * b.max_tiles;
+  g.tile_count = b.long_count + i;
+  return g;
+}
+
+// The short segments' list of a split plan (one kRowTile-row tile each).
+RowsGeom small_geom(const PlanBuffers& b, const moe_plan_t& P, int i, int64_t R) {
+  RowsGeom g;
+  g.tiles = b.small_tiles + (int64_t)i * P.E;
+  g.tile_count = b.small_count + i;
+  g.offsets = b.offsets + (int64_t)i * (P.E + 1);
+  g.grid_m = std::min<int64_t>(R, P.E);
+  g.row_tile = kRowTile;
   return g;
 }
 
@@ -206,12 +236,19 @@ MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const voi
     const int64_t R = (int64_t)P.k * g.n;
     const RowsGeom rg = rows_geom(pb, P, i, R);
     const int32_t* perm_i = pb.perm + g.pair_base;
+    // a split plan runs the gate/up product over its two split lists (the
+    // short segments' 128-row tiles and the rest) as one launch
+    const bool split = pb.small_tiles != nullptr;
+    const RowsGeom rgl = split ? long_geom(pb, P, i, R) : rg;
+    const RowsGeom rgs = split ? small_geom(pb, P, i, R) : rg;
+    const RowsGeom* gs = split ? &rgs : nullptr;
     if (fused) {
-      MOE_CHECK(gemm_up_swiglu(P.dtype, rg, X, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st,
-                               perm_i, P.k, P.N));
+      MOE_CHECK(gemm_up_swiglu(P.dtype, rgl, X, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st,
+                               perm_i, P.k, P.N, gs));
     } else {
       MOE_CHECK(launch_gather(P.dtype, X, xp, perm_i, R, P.k, P.N, P.H, st));
-      MOE_CHECK(gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st));
+      MOE_CHECK(gemm_up_swiglu(P.dtype, rgl, xp, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st,
+                               nullptr, 1, 0, gs));
     }
     MOE_CHECK(gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st));
     MOE_CHECK(launch_combine(P.dtype, o, pb.pos, gates, Y, P.N, P.K, i, g.n, P.k, P.H, st));
@@ -366,15 +403,19 @@ MOE_API int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk
     void* xp = ws + L.xp;
     void* o = ws + L.o;
     void* h = ws + L.h;
+    const bool split = pb.small_tiles != nullptr;  // the lists the forward call uses
+    const RowsGeom rgl = split ? long_geom(pb, P, chunk, R) : rg;
+    const RowsGeom rgs = split ? small_geom(pb, P, chunk, R) : rg;
+    const RowsGeom* gs = split ? &rgs : nullptr;
     switch (stage) {
       case MOE_STAGE_GATHER:
         err = launch_gather(P.dtype, X, xp, perm_i, R, P.k, P.N, P.H, st);
         break;
       case MOE_STAGE_GEMM_UP:
-        err = fused ? gemm_up_swiglu(P.dtype, rg, X, W_gate, W_up, h, nullptr, nullptr, P.H, P.F,
-                                     st, perm_i, P.k, P.N)
-                    : gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, nullptr, nullptr, P.H,
-                                     P.F, st);
+        err = fused ? gemm_up_swiglu(P.dtype, rgl, X, W_gate, W_up, h, nullptr, nullptr, P.H,
+                                     P.F, st, perm_i, P.k, P.N, gs)
+                    : gemm_up_swiglu(P.dtype, rgl, xp, W_gate, W_up, h, nullptr, nullptr, P.H,
+                                     P.F, st, nullptr, 1, 0, gs);
         break;
       case MOE_STAGE_GEMM_DOWN:
         err = gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st);

@@ -39,6 +39,17 @@ hipError_t down_bf16(const Params& p, dim3 grid, int bn, int rt, hipStream_t st)
   return launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, false, true, false, false, Epi::Store>(p, grid, st);
 }
 
+// Split plans: the 256-row tiles and the short segments' 128-row tiles of one
+// product in one launch.
+template <class G1>
+hipError_t up_pair(const Params& pb, int nb, const Params& ps, int ns, int bns, hipStream_t st) {
+  if (bns == 256)
+    return launch_lds_pair<G1, RowsGemm<Shape<128, 256, 2, 4, 32, 1>, true, true, false, false, Epi::SwiGLU>>(pb, nb, ps, ns, st);
+  if (bns == 128)
+    return launch_lds_pair<G1, RowsGemm<Shape<128, 128, 2, 4, 64, 1>, true, true, false, false, Epi::SwiGLU>>(pb, nb, ps, ns, st);
+  return hipErrorInvalidValue;
+}
+
 template <typename T>
 hipError_t up_swiglu_t(const Params& p, dim3 grid, int bn, bool save, hipStream_t st) {
   if (bn == 128) {
@@ -59,7 +70,7 @@ hipError_t down_t(const Params& p, dim3 grid, int bn, hipStream_t st) {
 
 hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const void* Wg,
                           const void* Wu, void* h, void* a, void* u, int H, int F, hipStream_t st,
-                          const int32_t* rows, int k, int64_t x_rows) {
+                          const int32_t* rows, int k, int64_t x_rows, const RowsGeom* gs) {
   if (g.grid_m == 0) return hipSuccess;
   Params p{};
   p.A = Xp; p.lda = H;
@@ -76,6 +87,15 @@ hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const vo
   const int bn = (dtype == MOE_BF16 && !save && !big && F % 256 == 0) ? 256 : (F % 128 == 0 ? 128 : 64);
   p.ntiles = F / bn;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
+  if (gs && dtype == MOE_BF16 && big && !save && bn == 128) {
+    Params ps = p;
+    ps.tiles = gs->tiles; ps.tile_count = gs->tile_count;
+    const int bns = F % 256 == 0 ? 256 : 128;
+    ps.ntiles = F / bns;
+    return up_pair<RowsGemm<Big<128>, true, true, false, false, Epi::SwiGLU>>(
+        p, (int)grid.x, ps, (int)(gs->grid_m * ps.ntiles), bns, st);
+  }
+  if (gs) return hipErrorInvalidValue;
   return dtype == MOE_BF16 ? up_swiglu_bf16(p, grid, bn, save, g.row_tile, st)
                            : up_swiglu_t<float>(p, grid, bn, save, st);
 }

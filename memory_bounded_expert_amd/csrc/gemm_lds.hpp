@@ -187,9 +187,11 @@ __device__ __forceinline__ int kswz(int r) {
   else return (r >> 2) & 3;
 }
 
+// The work-group's whole product.  bid is the work-group's index in a Rows
+// grid (a pair launch offsets the second product's ids); the other modes
+// read blockIdx themselves.
 template <Mode MODE, class S, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
-__global__ __launch_bounds__(64 * S::WGM * S::WGN)
-__attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void gemm_lds_kernel(const Params p) {
+__device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   using C = LdsCfg<S, DUAL>;
   using T = bf16_t;
   constexpr int BM = S::BM, BN = S::BN, BK = S::BK, NB = C::NB, NS = C::NS, CK = C::CK;
@@ -217,9 +219,8 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
   if constexpr (MODE == Mode::Rows) {
     // XCD-aware renumbering of the 1-D grid (xcd_contiguous)
     const int total = *p.tile_count * p.ntiles;
-    const int L = blockIdx.x;
-    if (L >= total) return;
-    const int lid = xcd_contiguous(L, total);
+    if (bid >= total) return;
+    const int lid = xcd_contiguous(bid, total);
     const int mt = lid / p.ntiles;
     n0 = (lid - mt * p.ntiles) * BN;
     const int2 tl = p.tiles[mt];
@@ -867,18 +868,67 @@ __attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void ge
 }
 
 template <Mode MODE, class S, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
+__global__ __launch_bounds__(64 * S::WGM * S::WGN)
+__attribute__((amdgpu_waves_per_eu(S::WG_PER_CU * S::WGM * S::WGN / 4))) void gemm_lds_kernel(const Params p) {
+  gemm_lds_body<MODE, S, DUAL, A_K, B_K, KCAT, EPI>(p, (int)blockIdx.x);
+}
+
+// One row-grouped product's template configuration, for the pair kernel.
+template <class S_, bool DUAL_, bool A_K_, bool B_K_, bool KCAT_, Epi EPI_>
+struct RowsGemm {
+  using S = S_;
+  using C = LdsCfg<S_, DUAL_>;
+  __device__ static __forceinline__ void run(const Params& p, int bid) {
+    gemm_lds_body<Mode::Rows, S_, DUAL_, A_K_, B_K_, KCAT_, EPI_>(p, bid);
+  }
+};
+
+// Two row-grouped products in one launch (the two tile lists of a split
+// chunk plan): work-groups [0, n1) run the first, the rest the second (n1 a
+// multiple of 8, so each id keeps its XCD).  Each product renumbers its own
+// ids, so both lists spread over all XCDs; renumbering the combined range
+// instead measured slower (one list's slower tiles then crowd some XCDs).
+template <class G1, class G2>
+__global__ __launch_bounds__(64 * G1::C::WAVES)
+__attribute__((amdgpu_waves_per_eu(G1::S::WG_PER_CU * G1::C::WAVES / 4))) void gemm_lds_pair_kernel(
+    const Params p1, const Params p2, int n1) {
+  static_assert(G1::C::WAVES == G2::C::WAVES && G1::S::WG_PER_CU == G2::S::WG_PER_CU,
+                "paired products need the same work-group shape");
+  const int b = (int)blockIdx.x;
+  if (b < n1)
+    G1::run(p1, b);
+  else
+    G2::run(p2, b - n1);
+}
+
+template <class KERN>
+hipError_t set_lds_attr(KERN kern, int lds, bool& done) {
+  if (done) return hipSuccess;  // per instantiation; benign race (idempotent)
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (err == hipSuccess) done = true;
+  return err;
+}
+
+template <Mode MODE, class S, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
 hipError_t launch_lds(const Params& p, dim3 grid, hipStream_t st) {
   using C = LdsCfg<S, DUAL>;
   auto kern = gemm_lds_kernel<MODE, S, DUAL, A_K, B_K, KCAT, EPI>;
-  const int lds = C::NS * C::STAGE;
-  static bool attr_set = false;  // per instantiation; benign race (idempotent)
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
-  kern<<<grid, C::THREADS, lds, st>>>(p);
+  static bool attr_set = false;
+  if (hipError_t err = set_lds_attr(kern, C::NS * C::STAGE, attr_set); err != hipSuccess) return err;
+  kern<<<grid, C::THREADS, C::NS * C::STAGE, st>>>(p);
+  return hipGetLastError();
+}
+
+// G1 over a 1-D Rows grid of n1 work-groups and G2 over n2, as one kernel.
+template <class G1, class G2>
+hipError_t launch_lds_pair(const Params& p1, int n1, const Params& p2, int n2, hipStream_t st) {
+  auto kern = gemm_lds_pair_kernel<G1, G2>;
+  constexpr int l1 = G1::C::NS * G1::C::STAGE, l2 = G2::C::NS * G2::C::STAGE;
+  constexpr int lds = l1 > l2 ? l1 : l2;
+  static bool attr_set = false;
+  if (hipError_t err = set_lds_attr(kern, lds, attr_set); err != hipSuccess) return err;
+  const int n1p = (n1 + 7) & ~7;  // ids n1..n1p-1 exit at once (past G1's tiles)
+  kern<<<dim3((unsigned)(n1p + n2)), G1::C::THREADS, lds, st>>>(p1, p2, n1p);
   return hipGetLastError();
 }
 

@@ -74,6 +74,16 @@ inline int row_tile_for(const moe_plan_t& p) {
              : kRowTile;
 }
 
+// The bf16 forward with kRowTileLarge tiles also lists its segments split: a
+// segment of at most kRowTile rows gets one kRowTile-row tile (a 256-row tile
+// over it leaves half its waves and loads idle), the others keep their
+// 256-row tiles (two 128-row tiles would stream their weights twice).  The
+// gate/up product runs the split lists as one launch; the down projection
+// stays on the one list of 256-row tiles, which measured faster for it.
+inline bool split_tiles(const moe_plan_t& p) {
+  return p.dtype == MOE_BF16 && row_tile_for(p) == kRowTileLarge;
+}
+
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct Layout {
   size_t logits = 0;      // [N][E] f32, forward only, when the caller passes none
@@ -83,6 +93,10 @@ struct Layout {
   size_t offsets = 0;     // [K][E+1] i32
   size_t tiles = 0;       // [K][max_tiles] int2 (expert, first row)
   size_t tile_count = 0;  // [K] i32
+  size_t small_tiles = 0; // [K][E] int2 forward with split tiles: short segments' tiles
+  size_t small_count = 0; // [K] i32
+  size_t long_tiles = 0;  // [K][max_tiles] int2 forward with split tiles: the other segments'
+  size_t long_count = 0;  // [K] i32
   size_t perm = 0;        // [N*k] i32
   size_t pos = 0;         // [N*k] i32
   size_t xp = 0;          // [k c_eff][H]  permuted inputs (dispatch buffer 1)
@@ -98,6 +112,7 @@ struct Layout {
   int64_t nblk = 0;
   int64_t max_tiles = 0;
   int row_tile = kRowTile;
+  bool split = false;     // small_tiles / small_count present
 };
 
 enum class Pass { Forward, Backward, Debug };
@@ -121,6 +136,10 @@ struct PlanBuffers {
   int64_t nblk;
   int64_t max_tiles;
   int row_tile;
+  int2* small_tiles;     // nullptr: one tile list (split_tiles)
+  int32_t* small_count;
+  int2* long_tiles;
+  int32_t* long_count;
 };
 // Plans every chunk at once: counts, scans and scatters the whole batch's
 // routed pairs (O(N k) int32, nothing H-wide).  3 launches.
@@ -160,9 +179,13 @@ struct RowsGeom {
 // h = silu(Xp W_gate[e]) * (Xp W_up[e]) per expert segment; save_au also
 // stores a and u.  With rows != nullptr (bf16 only), Xp is not a buffer:
 // row r is row rows[r] / k of X (x_rows rows), read straight from X.
+// With gs (a split plan's short-segment list, bf16 forward only), g (then
+// the split plan's long-segment list) in 256-row tiles and gs in 128-row
+// tiles run as one launch.
 hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const void* Wg,
                           const void* Wu, void* h, void* a, void* u, int H, int F, hipStream_t st,
-                          const int32_t* rows = nullptr, int k = 1, int64_t x_rows = 0);
+                          const int32_t* rows = nullptr, int k = 1, int64_t x_rows = 0,
+                          const RowsGeom* gs = nullptr);
 // O = h W_down[e]
 hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd, void* O, int H,
                      int F, hipStream_t st);

@@ -68,12 +68,20 @@ __device__ int block_inclusive_scan(int v, int* buf) {
   return r;
 }
 
+// tiles: every segment in row_tile-row tiles.  With small_tiles set, the
+// same segments are also listed split: a segment of 1..kRowTile rows gets one
+// kRowTile-row tile in small_tiles (at most E per chunk), a longer one its
+// row_tile-row tiles in long_tiles.
 __global__ __launch_bounds__(kThreads) void plan_scan_kernel(int32_t* __restrict__ blk, int E,
                                                              int64_t nblk,
                                                              int32_t* __restrict__ offsets,
                                                              int2* __restrict__ tiles,
                                                              int32_t* __restrict__ tile_count,
-                                                             int64_t max_tiles, int row_tile) {
+                                                             int64_t max_tiles, int row_tile,
+                                                             int2* __restrict__ small_tiles,
+                                                             int32_t* __restrict__ small_count,
+                                                             int2* __restrict__ long_tiles,
+                                                             int32_t* __restrict__ long_count) {
   __shared__ int tot[kMaxE];
   __shared__ int eoff[kMaxE];
   __shared__ int buf[kThreads];
@@ -95,26 +103,46 @@ __global__ __launch_bounds__(kThreads) void plan_scan_kernel(int32_t* __restrict
   const int seg = (E + kThreads - 1) / kThreads;
   const int e0 = tid * seg;
   const int e1 = min(E, e0 + seg);
-  int rows = 0, ntile = 0;
+  const bool split = small_tiles != nullptr;
+  auto is_small = [&](int m) { return split && m > 0 && m <= kRowTile; };
+  int rows = 0, ntile = 0, nsmall = 0, nlong = 0;
   for (int e = e0; e < e1; ++e) {
     rows += tot[e];
-    ntile += (tot[e] + row_tile - 1) / row_tile;
+    const int nt = (tot[e] + row_tile - 1) / row_tile;
+    ntile += nt;
+    if (is_small(tot[e]))
+      ++nsmall;
+    else
+      nlong += nt;
   }
   int row_run = block_inclusive_scan(rows, buf) - rows;
   int tile_run = block_inclusive_scan(ntile, buf) - ntile;
+  int small_run = block_inclusive_scan(nsmall, buf) - nsmall;
+  int long_run = block_inclusive_scan(nlong, buf) - nlong;
   int32_t* off = offsets + (int64_t)i * (E + 1);
   int2* tl = tiles + (int64_t)i * max_tiles;
+  int2* ll = split ? long_tiles + (int64_t)i * max_tiles : nullptr;
   for (int e = e0; e < e1; ++e) {
     off[e] = row_run;
     eoff[e] = row_run;
     const int nt = (tot[e] + row_tile - 1) / row_tile;
     for (int q = 0; q < nt; ++q) tl[tile_run + q] = make_int2(e, row_run + q * row_tile);
-    row_run += tot[e];
     tile_run += nt;
+    if (is_small(tot[e])) {
+      small_tiles[(int64_t)i * E + small_run++] = make_int2(e, row_run);
+    } else if (split) {
+      for (int q = 0; q < nt; ++q) ll[long_run + q] = make_int2(e, row_run + q * row_tile);
+      long_run += nt;
+    }
+    row_run += tot[e];
   }
   if (tid == kThreads - 1) {
     off[E] = row_run;
     tile_count[i] = tile_run;
+    if (split) {
+      small_count[i] = small_run;
+      long_count[i] = long_run;
+    }
   }
   __syncthreads();
   for (int e = tid; e < E; e += kThreads) {
@@ -154,7 +182,8 @@ hipError_t launch_plan(const int32_t* idx, int64_t N, int K, int k, int E, const
                       (size_t)E * sizeof(unsigned long long), st>>>(idx, N, K, k, E, b.nblk,
                                                                     b.blk, b.rank);
   plan_scan_kernel<<<K, kThreads, 0, st>>>(b.blk, E, b.nblk, b.offsets, b.tiles, b.tile_count,
-                                           b.max_tiles, b.row_tile);
+                                           b.max_tiles, b.row_tile, b.small_tiles,
+                                           b.small_count, b.long_tiles, b.long_count);
   const int64_t pairs = N * k;
   plan_scatter_kernel<<<(unsigned)ceil_div(pairs, kThreads), kThreads, 0, st>>>(
       idx, N, K, k, E, b.nblk, b.blk, b.rank, b.perm, b.pos);
