@@ -88,13 +88,20 @@ __global__ __launch_bounds__(kThreads) void plan_scan_kernel(int32_t* __restrict
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
   int32_t* base = blk + (int64_t)i * nblk * E;
-  // per-expert exclusive prefix over the chunk's blocks, in place
+  // per-expert exclusive prefix over the chunk's blocks, in place; the counts
+  // are read eight blocks ahead of the writes so the reads overlap
+  constexpr int kAhead = 8;
   for (int e = tid; e < E; e += kThreads) {
     int run = 0;
-    for (int64_t b = 0; b < nblk; ++b) {
-      const int c = base[b * E + e];
-      base[b * E + e] = run;
-      run += c;
+    for (int64_t b0 = 0; b0 < nblk; b0 += kAhead) {
+      int c[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) c[u] = b0 + u < nblk ? base[(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) {
+        if (b0 + u < nblk) base[(b0 + u) * E + e] = run;
+        run += c[u];
+      }
     }
     tot[e] = run;
   }
@@ -147,7 +154,14 @@ __global__ __launch_bounds__(kThreads) void plan_scan_kernel(int32_t* __restrict
   __syncthreads();
   for (int e = tid; e < E; e += kThreads) {
     const int o = eoff[e];
-    for (int64_t b = 0; b < nblk; ++b) base[b * E + e] += o;
+    for (int64_t b0 = 0; b0 < nblk; b0 += kAhead) {
+      int c[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) c[u] = b0 + u < nblk ? base[(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u)
+        if (b0 + u < nblk) base[(b0 + u) * E + e] = c[u] + o;
+    }
   }
 }
 
