@@ -11,7 +11,9 @@ fp64 oracle:
     tokens;
   * the full-size case (8192 tokens, H 7168, V 200,000, strips of 8192) on
     sampled tokens and vocabulary rows, in the launch configuration the
-    benchmark times, and its strip-width invariance against strips of 65,536.
+    benchmark times, and its strip-width invariance against strips of 65,536;
+  * the per-kernel debug stages, re-launched in pipeline order, reproduce
+    the calls' outputs bitwise.
 
 Tolerances: every output within 1e-2 of max|oracle| (the bf16 bound of the
 layer's contract).  The loss and log-normaliser are also held to 1e-3: the
@@ -196,3 +198,28 @@ def test_full_size_sampled(full_inputs):
     other = run(d, 65536, dloss=gd)
     assert same_bits(out, other), "strip width changed the full-size result"
     say("[full] strips of 65,536: bitwise identical")
+
+
+def test_debug_stages_replay_the_calls():
+    # re-launching every strip's kernels in pipeline order through
+    # cce_debug_stage reproduces the calls' outputs bitwise (the benchmark's
+    # per-kernel timings rely on it)
+    require_lib()
+    wl = SMALL.with_(name="stages", N=300, H=256, V=3000, v_chunk=1024)
+    inp = datagen.CeInputs(wl)
+    d = CeDev(inp)
+    plan = B.cce_plan(wl.N, wl.H, wl.V, wl.v_chunk)
+    wsf, wsb = B.workspace(plan, "fwd", DEV), B.workspace(plan, "bwd", DEV)
+    loss, lse = B.cce_forward(plan, d.X, d.W, d.t, ws=wsf)
+    dX, dW = B.cce_backward(plan, d.X, d.W, d.t, lse, d.dloss, ws=wsb)
+    torch.cuda.synchronize()
+    loss0, lse0, dW0 = loss.clone(), lse.clone(), dW.clone()
+    loss.zero_(); lse.zero_(); dW.zero_()
+    for s in range(plan.S):
+        for st in ("logits", "fold"):
+            B.cce_debug_stage(plan, st, s, d.X, d.W, d.t, loss, lse, d.dloss, dX, dW, wsf)
+    for s in range(plan.S):
+        for st in ("grad", "dx", "dw"):
+            B.cce_debug_stage(plan, st, s, d.X, d.W, d.t, loss, lse, d.dloss, dX, dW, wsb)
+    torch.cuda.synchronize()
+    assert torch.equal(loss, loss0) and torch.equal(lse, lse0) and torch.equal(dW, dW0)

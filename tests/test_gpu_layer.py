@@ -224,3 +224,21 @@ def test_grouped_row_tiles_bf16():
     plan = plan_for(wl)
     assert plan.K == 2 and plan.c_eff == 1024
     run_workload(wl.name, full=False, wl=wl, reduced=(wl.N, wl.c))
+
+
+# Chunks averaging ~125 rows per expert take 256-row tiles, and the forward's
+# gate/up GEMM then runs the chunk's segments as two lists in one launch:
+# segments of at most 128 rows in 128-row tiles, longer ones in 256-row tiles.
+# K = 2 chunks of 1000 tokens over 16 experts, top-2: segments straddle 128
+# rows, so both lists are populated; the unchunked comparison run (about 250
+# rows per expert) is split too, with other segments in each list.
+SPLIT_TILES = datagen.WORKLOADS["train_bf16"].with_(
+    name="split_tiles_bf16", N=2000, H=256, E=16, k=2, F=256, c=1000, K_max=16)
+
+
+def test_split_tile_lists_bf16():
+    wl = SPLIT_TILES
+    plan = plan_for(wl)
+    assert plan.K == 2 and plan.c_eff == 1000
+    assert wl.k * plan.c_eff >= 96 * wl.E  # 256-row tiles, hence the split lists
+    run_workload(wl.name, full=False, wl=wl, reduced=(wl.N, wl.c))
