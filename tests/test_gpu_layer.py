@@ -9,7 +9,12 @@ For each workload:
     gradients of sampled experts) evaluated one by one by the oracle;
   * chunked == unchunked: the same call with K_max = 1 gives bitwise equal
     per-token outputs; two runs give bitwise equal results;
-  * the dispatch buffers stay within 2 k c_eff H b.
+  * the dispatch buffers stay within 2 k c_eff H b (half of it when the bf16
+    forward reads its permuted rows from X inside the GEMM).
+
+Beyond the named workloads: grouped expert tiles, the split tile lists of
+short segments, and a batch whose X is too large for the in-GEMM gather, so
+the forward gathers into its own buffer.
 """
 
 import numpy as np
@@ -125,10 +130,12 @@ def run_workload(name, full=True, wl=None, reduced=None):
     err = rel_err(dev_to_f64(Y[torch.from_numpy(toks).to(DEV)]), Yt)
     say(f"[{name}] full Y rel err on {len(toks)} sampled tokens {err:.3e}")
     assert err <= tol
-    # the bf16 forward reads its permuted inputs straight from X: one H-wide
-    # buffer (the expert outputs) instead of the bound's two
+    # the bf16 forward reads its permuted inputs straight from X (when X fits
+    # one buffer resource's 32-bit offsets): one H-wide buffer (the expert
+    # outputs) instead of the bound's two
     bound = oracle.dispatch_bound_bytes(wl.k, plan.c_eff, wl.H, b)
-    assert st["dispatch_bytes"] == (bound // 2 if wl.dtype == "bf16" else bound)
+    in_place = wl.dtype == "bf16" and wl.N * wl.H * 2 <= 0x7FFFFFF0
+    assert st["dispatch_bytes"] == (bound // 2 if in_place else bound)
     Y2, idx2, g2, lg2, _ = forward(d, plan)
     assert torch.equal(Y, Y2) and torch.equal(idx, idx2) and torch.equal(lg, lg2)
     del Y2, idx2, g2, lg2
@@ -242,3 +249,22 @@ def test_split_tile_lists_bf16():
     assert plan.K == 2 and plan.c_eff == 1000
     assert wl.k * plan.c_eff >= 96 * wl.E  # 256-row tiles, hence the split lists
     run_workload(wl.name, full=False, wl=wl, reduced=(wl.N, wl.c))
+
+
+# X of 2^31 bytes or more does not fit one buffer resource, so the bf16
+# forward gathers the permuted rows into their buffer (two H-wide buffers, the
+# whole bound) instead of reading them from X inside the GEMM.  524,800 tokens
+# of H = 2048 (X = 2.15 GB), 128 experts under Zipf(1.2) routing, top-2, in
+# K = 8 chunks of 65,600 tokens: 256-row tiles with the split lists (the
+# coldest experts keep segments of at most 128 rows).  Forward only: the
+# backward always gathers.
+UNFUSED = datagen.WORKLOADS["zipf_bf16"].with_(
+    name="unfused_gather_bf16", N=524800, H=2048, E=128, k=2, F=128, c=65600, K_max=8)
+
+
+def test_unfused_gather_bf16():
+    wl = UNFUSED
+    plan = plan_for(wl)
+    assert plan.K == 8 and plan.c_eff == 65600
+    assert wl.N * wl.H * 2 > 0x7FFFFFF0 and wl.k * plan.c_eff >= 96 * wl.E
+    run_workload(wl.name, full=True, wl=wl, reduced=(2000, 500))
