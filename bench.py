@@ -264,6 +264,46 @@ def cce_main(args, datagen, np, torch, B):
     print(json.dumps(out), flush=True)
 
 
+def blas_yardstick(torch, wl, plan, stages):
+    """torch.bmm (the vendor BLAS) on one chunk's expert products with every
+    expert given the same number of rows, stored contiguously: E x [m, H] x
+    [H, 2F] for gate and up side by side, E x [m, F] x [F, H] for the down
+    projection, m = k c_eff / E rounded down to a multiple of 16.  No gather,
+    no SwiGLU, no ragged segments: a plain-GEMM reference point for the
+    grouped GEMMs' times on the same shapes."""
+    dev = torch.device("cuda:0")
+    E, H, F = wl.E, wl.H, wl.F
+    m = max(16, (wl.k * plan.c_eff // E) // 16 * 16)
+    g = torch.Generator(device=dev).manual_seed(7)
+    bf = torch.bfloat16
+    A = torch.randn(E, m, H, device=dev, dtype=bf, generator=g)
+    Wgu = torch.randn(E, H, 2 * F, device=dev, dtype=bf, generator=g)
+    Hh = torch.randn(E, m, F, device=dev, dtype=bf, generator=g)
+    Wd = torch.randn(E, F, H, device=dev, dtype=bf, generator=g)
+    res = {"rows_per_expert": m}
+    for name, fn, flops in (("gemm_up", lambda: torch.bmm(A, Wgu), 4.0 * E * m * H * F),
+                            ("gemm_down", lambda: torch.bmm(Hh, Wd), 2.0 * E * m * H * F)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        ours = stages[name]
+        res[name] = {"bmm_us": round(us, 2), "bmm_TFLOP_per_s": round(flops / us / 1e6, 1),
+                     "grouped_us": ours["us_per_launch"],
+                     "grouped_TFLOP_per_s": ours.get("TFLOP_per_s")}
+        log(f"  yardstick {name}: torch.bmm {us:.1f} us ({flops / us / 1e6:.0f} TFLOP/s) on "
+            f"{E} x [{m} rows]; grouped GEMM {ours['us_per_launch']} us")
+    del A, Wgu, Hh, Wd
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,6 +316,10 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=5)
     ap.add_argument("--backward", action="store_true",
                     help="also time forward+backward steps (reported under forward_backward)")
+    ap.add_argument("--blas-yardstick", action="store_true",
+                    help="also time the vendor library's batched GEMM (torch.bmm) on one chunk's "
+                         "expert products with equal, contiguous row groups (reported under "
+                         "blas_yardstick; context for the grouped GEMMs, not part of the step)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -440,6 +484,8 @@ def main():
                      for s in ("gemm_up", "gemm_down"))
     gemm_us = sum(stages[s]["us_per_launch"] * K for s in ("gemm_up", "gemm_down"))
 
+    yard = blas_yardstick(torch, wl, plan, stages) if args.blas_yardstick and bf else None
+
     fb = None
     if args.backward:
         # one step = forward (routing saved) + backward with per-chunk recompute:
@@ -507,6 +553,7 @@ def main():
                    "c": wl.c, "K_max": wl.K_max, "K": K, "c_eff": plan.c_eff,
                    "parallelism": "single GPU"},
         "forward_backward": fb,
+        "blas_yardstick": yard,
         "roofline": roof,
         "grouped_gemm": {"TFLOP_per_s": round(gemm_flops / gemm_us / 1e6, 1),
                          "mfma_frac": round(gemm_flops / gemm_us / 1e6 / peak_tf, 4)},
