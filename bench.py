@@ -85,12 +85,12 @@ def stage_work(stage, wl, b, n_i, R_i, E_i):
     H, F = wl.H, wl.F
     if stage == "gemm_up":
         return (2 * E_i * H * F * b + R_i * H * b + R_i * F * b), 4.0 * R_i * H * F
-    if stage == "gemm_down":
-        return (E_i * F * H * b + R_i * F * b + R_i * H * b), 2.0 * R_i * H * F
+    if stage == "gemm_down":  # (plus each row's pair index and gate)
+        return (E_i * F * H * b + R_i * F * b + R_i * H * b + R_i * 8), 2.0 * R_i * H * F
     if stage == "gather":  # read each token once, write its k rows
         return (n_i + R_i) * H * b, 0.0
-    if stage == "combine":  # read k rows, their gates and rows, write the token
-        return (R_i + n_i) * H * b + R_i * 8, 2.0 * R_i * H
+    if stage == "combine":  # read the k gate-scaled rows and their positions, write the token
+        return (R_i + n_i) * H * b + R_i * 4, 1.0 * R_i * H
     raise KeyError(stage)
 
 

@@ -53,6 +53,7 @@ Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_d
   if (pass != Pass::Debug) {
     L.perm = take(N * k * 4);
     L.pos = take(N * k * 4);
+    if (pass == Pass::Forward) L.row_gates = take(N * k * 4);
     const size_t rows = k * ce;
     // the bf16 forward reads its permuted inputs straight from X
     if (pass == Pass::Backward || !fused_gather(p)) L.xp = take(rows * H * b);
@@ -89,6 +90,7 @@ PlanBuffers plan_buffers(char* ws, const Layout& L, int32_t* offsets, int32_t* p
   b.tile_count = (int32_t*)(ws + L.tile_count);
   b.perm = perm ? perm : (int32_t*)(ws + L.perm);
   b.pos = pos ? pos : (int32_t*)(ws + L.pos);
+  b.row_gates = L.row_gates ? (float*)(ws + L.row_gates) : nullptr;
   b.nblk = L.nblk;
   b.max_tiles = L.max_tiles;
   b.row_tile = L.row_tile;
@@ -225,7 +227,7 @@ MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const voi
   MOE_CHECK(gemm_router(P.dtype, X, W_r, router_bias, lg, P.N, P.H, P.E, st, rparts, rs));
   MOE_CHECK(launch_topk(lg, P.N, P.E, P.k, topk_idx, gates, st, rparts, rs, router_bias));
   const PlanBuffers pb = plan_buffers(ws, L, nullptr, nullptr, nullptr);
-  MOE_CHECK(launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st));
+  MOE_CHECK(launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st, gates));
   launches += 2;
   const bool fused = fused_gather(P);
   void* xp = ws + L.xp;
@@ -250,8 +252,10 @@ MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const voi
       MOE_CHECK(gemm_up_swiglu(P.dtype, rgl, xp, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st,
                                nullptr, 1, 0, gs));
     }
-    MOE_CHECK(gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st));
-    MOE_CHECK(launch_combine(P.dtype, o, pb.pos, gates, Y, P.N, P.K, i, g.n, P.k, P.H, st));
+    // the gates scale the expert rows in the down projection's epilogue; the
+    // combine then sums each token's k rows
+    MOE_CHECK(gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st, pb.row_gates + g.pair_base));
+    MOE_CHECK(launch_combine(P.dtype, o, pb.pos, Y, P.N, P.K, i, g.n, P.k, P.H, st));
   }
   fill_stats(stats, P, launches, L.total,
              (size_t)P.k * P.c_eff * P.F * elem_bytes(P.dtype), fused ? 1 : 2);
@@ -394,7 +398,7 @@ MOE_API int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk
   } else if (stage == MOE_STAGE_TOPK) {
     err = launch_topk(lg, P.N, P.E, P.k, topk_idx, gates, st, rparts, rs, router_bias);
   } else if (stage == MOE_STAGE_PLAN) {
-    err = launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st);
+    err = launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st, gates);
   } else {
     const ChunkGeom g = chunk_geom(P.N, P.K, P.k, chunk);
     const int64_t R = (int64_t)P.k * g.n;
@@ -418,10 +422,10 @@ MOE_API int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk
                                      P.F, st, nullptr, 1, 0, gs);
         break;
       case MOE_STAGE_GEMM_DOWN:
-        err = gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st);
+        err = gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st, pb.row_gates + g.pair_base);
         break;
       default:
-        err = launch_combine(P.dtype, o, pb.pos, gates, Y, P.N, P.K, chunk, g.n, P.k, P.H, st);
+        err = launch_combine(P.dtype, o, pb.pos, Y, P.N, P.K, chunk, g.n, P.k, P.H, st);
     }
   }
   return err == hipSuccess ? MOE_OK : MOE_EHIP;

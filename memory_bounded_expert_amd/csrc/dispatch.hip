@@ -37,12 +37,12 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
   }
 }
 
-// Y[t] = sum_{s<k} g[t,s] O[pos[t,s]] for the tokens of chunk i; fp32 sum in
-// slot order, one rounding at the store.
+// Y[t] = sum_{s<k} O[pos[t,s]] for the tokens of chunk i, the rows already
+// scaled by their gates in the down projection's epilogue; fp32 sum in slot
+// order, one rounding at the store.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__ O,
                                                            const int32_t* __restrict__ pos,
-                                                           const float* __restrict__ gates,
                                                            T* __restrict__ Y, int K, int i,
                                                            int64_t n_i, int k, int H) {
   constexpr int EPC = Elem<T>::kPer16B;
@@ -61,12 +61,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__
     constexpr int SB = 8;
     for (int s0 = 0; s0 < k; s0 += SB) {
       u32x4_t raw[SB];
-      float g[SB];
 #pragma unroll
       for (int u = 0; u < SB; ++u) {
         if (s0 + u < k) {
           const int64_t r = pos[t * k + s0 + u];
-          g[u] = gates[t * k + s0 + u];
           raw[u] = reinterpret_cast<const u32x4_t*>(O + r * H)[c];
         }
       }
@@ -76,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__
           float v[EPC];
           unpack16(raw[u], v, T());
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[e] = fmaf(g[u], v[e], acc[e]);
+          for (int e = 0; e < EPC; ++e) acc[e] += v[e];
         }
       }
     }
@@ -321,17 +319,17 @@ hipError_t launch_gather(int dtype, const void* src, void* dst, const int32_t* p
   return hipGetLastError();
 }
 
-hipError_t launch_combine(int dtype, const void* O, const int32_t* pos, const float* gates, void* Y,
-                          int64_t N, int K, int i, int64_t n_i, int k, int H, hipStream_t st) {
+hipError_t launch_combine(int dtype, const void* O, const int32_t* pos, void* Y, int64_t N, int K,
+                          int i, int64_t n_i, int k, int H, hipStream_t st) {
   (void)N;
   if (n_i == 0) return hipSuccess;
   const int64_t chunks = n_i * H * elem_bytes(dtype) / 16;
   const unsigned grid = grid_for(chunks, kThreads);
   if (dtype == MOE_BF16)
-    combine_kernel<bf16_t><<<grid, kThreads, 0, st>>>((const bf16_t*)O, pos, gates, (bf16_t*)Y, K,
-                                                      i, n_i, k, H);
+    combine_kernel<bf16_t><<<grid, kThreads, 0, st>>>((const bf16_t*)O, pos, (bf16_t*)Y, K, i, n_i,
+                                                      k, H);
   else
-    combine_kernel<float><<<grid, kThreads, 0, st>>>((const float*)O, pos, gates, (float*)Y, K, i,
+    combine_kernel<float><<<grid, kThreads, 0, st>>>((const float*)O, pos, (float*)Y, K, i,
                                                      n_i, k, H);
   return hipGetLastError();
 }

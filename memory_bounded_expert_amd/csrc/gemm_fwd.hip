@@ -101,12 +101,13 @@ hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const vo
 }
 
 hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd, void* O, int H,
-                     int F, hipStream_t st) {
+                     int F, hipStream_t st, const float* row_gates) {
   if (g.grid_m == 0) return hipSuccess;
   Params p{};
   p.A = h; p.lda = F;
   p.B = Wd; p.ldb = H; p.b_estride = (int64_t)F * H;
   p.C = O; p.ldc = H;
+  p.row_scale = row_gates;
   p.N = H; p.K = F;
   p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
   const int bn = g.row_tile == kRowTileLarge ? (H % 256 == 0 ? 256 : 128)

@@ -100,6 +100,10 @@ struct Params {
   float* sw_dgp;
   int64_t sw_rows;
   int64_t sw_nk;
+  // Epi::Store in Mode::Rows: row r (of the chunk) is multiplied by
+  // row_scale[r] in fp32 before its one rounding (nullptr: unscaled).  The
+  // down projection passes its rows' gates.
+  const float* row_scale;
 };
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
@@ -524,7 +528,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
         const int64_t o = (int64_t)grow * p.ldc + gcol;
         const float v0 = acc[0][i][j][q];
         if constexpr (EPI == Epi::Store) {
-          static_cast<T*>(p.C)[o] = Elem<T>::from_f(v0);
+          float gv = 1.f;
+          if constexpr (MODE == Mode::Rows) {
+            if (p.row_scale) gv = p.row_scale[grow];
+          }
+          static_cast<T*>(p.C)[o] = Elem<T>::from_f(v0 * gv);
         } else if constexpr (EPI == Epi::SwiGLU || EPI == Epi::SwiGLUSave) {
           const float v1 = acc[NB - 1][i][j][q];
           // silu with the hardware exp and reciprocal (about 1 ulp each)

@@ -521,6 +521,16 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   // of the final iteration hits such a copy and is not used.  The loop is
   // unrolled so that every stage index and register set is a compile-time
   // constant.
+  // Row scales of a scaled store, one per lane (the wave's row slice is at
+  // most 64 rows): requested before the pipeline's first loads, so they
+  // have landed long before the epilogue reads them
+  float row_scale_lane = 1.f;
+  if constexpr (MODE == Mode::Rows && EPI == Epi::Store) {
+    static_assert(WM <= 64, "one row scale per lane");
+    const int row = m0 + wm * WM + lane;
+    if (p.row_scale && lane < WM && row < row_end) row_scale_lane = p.row_scale[row];
+  }
+
   constexpr int U = (NS % 2 == 0) ? NS : 2 * NS;
   if (nk > 0) {  // (an expert with no rows in store mode skips to the epilogue)
   const int last = nk - 1;
@@ -795,7 +805,15 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
       }
     };
     if constexpr (EPI == Epi::Store) {
-      stage_store(static_cast<T*>(p.C), [&](int i, int j, int q) { return f2bf(acc[0][i][j][q]); });
+      // each row times its scale (the down projection's gates; 1 without
+      // row_scale, which leaves the value unchanged), then rounded once.
+      // Lane l loaded the scale of the wave's row l before the pipeline.
+      float rg[FM][4];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rg[i][q] = __shfl(row_scale_lane, i * 16 + 4 * lg + q, 64);
+      stage_store(static_cast<T*>(p.C), [&](int i, int j, int q) { return f2bf(acc[0][i][j][q] * rg[i][q]); });
     } else if constexpr (EPI == Epi::CEGrad) {
       // Vocabulary-strip cross-entropy, backward: the strip's logit gradient
       // dl_row (exp(logit - lse_row) - [column == target_row]), bf16;

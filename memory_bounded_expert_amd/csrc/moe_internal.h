@@ -99,6 +99,7 @@ struct Layout {
   size_t long_count = 0;  // [K] i32
   size_t perm = 0;        // [N*k] i32
   size_t pos = 0;         // [N*k] i32
+  size_t row_gates = 0;   // [N*k] f32 forward: gates in permuted-row order
   size_t xp = 0;          // [k c_eff][H]  permuted inputs (dispatch buffer 1)
   size_t o = 0;           // [k c_eff][H]  expert outputs / dY rows, then dXp (buffer 2)
   size_t h = 0;           // [k c_eff][F]  h (forward); h, then g*h (backward)
@@ -133,6 +134,7 @@ struct PlanBuffers {
   int32_t* tile_count;
   int32_t* perm;
   int32_t* pos;
+  float* row_gates;      // [N*k] gate of each permuted row (forward), or nullptr
   int64_t nblk;
   int64_t max_tiles;
   int row_tile;
@@ -143,14 +145,17 @@ struct PlanBuffers {
 };
 // Plans every chunk at once: counts, scans and scatters the whole batch's
 // routed pairs (O(N k) int32, nothing H-wide).  3 launches.
+// With b.row_gates set, also writes each permuted row's gate (gates [N*k]).
 hipError_t launch_plan(const int32_t* idx, int64_t N, int K, int k, int E, const PlanBuffers& b,
-                       hipStream_t st);
+                       hipStream_t st, const float* gates = nullptr);
 
 // Data movement (dtype-dispatched: 0 f32, 1 bf16).
 hipError_t launch_gather(int dtype, const void* src, void* dst, const int32_t* perm_chunk, int64_t R,
                          int k, int64_t N, int H, hipStream_t st);
-hipError_t launch_combine(int dtype, const void* O, const int32_t* pos, const float* gates, void* Y,
-                          int64_t N, int K, int i, int64_t n_i, int k, int H, hipStream_t st);
+// Y[t] = sum_s O[pos[t, s]] over the k gate-scaled expert rows of each token
+// of chunk i.
+hipError_t launch_combine(int dtype, const void* O, const int32_t* pos, void* Y, int64_t N, int K,
+                          int i, int64_t n_i, int k, int H, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_transpose(int dtype, const void* src, void* dst, int rows, int cols,
                             hipStream_t st);
@@ -186,9 +191,10 @@ hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const vo
                           const void* Wu, void* h, void* a, void* u, int H, int F, hipStream_t st,
                           const int32_t* rows = nullptr, int k = 1, int64_t x_rows = 0,
                           const RowsGeom* gs = nullptr);
-// O = h W_down[e]
+// O[r] = row_gates[r] (h[r] W_down[e]): each chunk row scaled by its pair's
+// gate before the one rounding (row_gates as the planner lays them out).
 hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd, void* O, int H,
-                     int F, hipStream_t st);
+                     int F, hipStream_t st, const float* row_gates);
 // dh = dYp W_down[e]^T (fp32 out)
 hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd, float* dh, int H,
                    int F, hipStream_t st);

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void plan_scan_kernel(int32_t* __restrict
 __global__ __launch_bounds__(kThreads) void plan_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t N, int K, int k, int E, int64_t nblk,
     const int32_t* __restrict__ base, const int32_t* __restrict__ rank, int32_t* __restrict__ perm,
-    int32_t* __restrict__ pos) {
+    int32_t* __restrict__ pos, const float* __restrict__ gates, float* __restrict__ row_gates) {
   const int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (p >= N * k) return;
   const int64_t t = p / k;
@@ -185,12 +185,14 @@ __global__ __launch_bounds__(kThreads) void plan_scatter_kernel(
   const int64_t q = N / K, rem = N % K;
   const int64_t pb = (int64_t)k * (i * q + (i < rem ? i : rem));
   perm[pb + r] = (int32_t)p;
+  if (row_gates) row_gates[pb + r] = gates[p];
 }
 
 }  // namespace
 
 hipError_t launch_plan(const int32_t* idx, int64_t N, int K, int k, int E, const PlanBuffers& b,
-                       hipStream_t st) {
+                       hipStream_t st, const float* gates) {
+  if (b.row_gates && !gates) return hipErrorInvalidValue;
   if (N == 0) return hipSuccess;
   plan_count_kernel<<<dim3((unsigned)b.nblk, (unsigned)K), kPlanBlock,
                       (size_t)E * sizeof(unsigned long long), st>>>(idx, N, K, k, E, b.nblk,
@@ -200,7 +202,7 @@ hipError_t launch_plan(const int32_t* idx, int64_t N, int K, int k, int E, const
                                            b.small_count, b.long_tiles, b.long_count);
   const int64_t pairs = N * k;
   plan_scatter_kernel<<<(unsigned)ceil_div(pairs, kThreads), kThreads, 0, st>>>(
-      idx, N, K, k, E, b.nblk, b.blk, b.rank, b.perm, b.pos);
+      idx, N, K, k, E, b.nblk, b.blk, b.rank, b.perm, b.pos, gates, b.row_gates);
   return hipGetLastError();
 }
 
