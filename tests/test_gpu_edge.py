@@ -6,6 +6,12 @@ through the C ABI, against the full fp64 oracle (forward and backward):
   * a single token (one chunk of one row per selected expert), fp32;
   * 64 experts with 20 tokens of top-2: most experts have no rows in a chunk;
   * k = 1 (every gate exactly 1);
+  * one token per chunk (c = 1, K = N);
+  * K_max binding: c = 10 asks for 100 chunks, K_max = 3 gives c_eff = 334;
+  * every token routed to the same two experts (a Zipf(12) router bias over
+    8 experts with top-2): two full segments per chunk, six empty experts;
+  * the largest k: k = E = 64, every token in every expert;
+  * fp32 with k = E = 4;
   * N = 0: both entry points succeed and enqueue nothing but the weight
     gradients' zero fill.
 
@@ -35,6 +41,19 @@ CASES = {
                                     c=6, K_max=8),
     # k = 1
     "top1_bf16": BF.with_(name="top1_bf16", N=50, H=64, E=8, k=1, F=64, c=16, K_max=4),
+    # c = 1: nine chunks of one token
+    "one_token_per_chunk_bf16": BF.with_(name="one_token_per_chunk_bf16", N=9, H=64, E=8, k=2,
+                                         F=64, c=1, K_max=16),
+    # K_max binds: K = 3 chunks of 334, 333, 333 tokens
+    "kmax_binds_bf16": BF.with_(name="kmax_binds_bf16", N=1000, H=128, E=16, k=4, F=128, c=10,
+                                K_max=3),
+    # all routing on two experts: segments of a whole chunk, the rest empty
+    "two_hot_experts_bf16": BF.with_(name="two_hot_experts_bf16", N=600, H=128, E=8, k=2, F=128,
+                                     c=300, K_max=4, zipf_s=12.0),
+    # k = E = 64
+    "k64_bf16": BF.with_(name="k64_bf16", N=10, H=64, E=64, k=64, F=64, c=4, K_max=4),
+    # fp32, k = E = 4
+    "k_eq_E_f32": F32.with_(name="k_eq_E_f32", N=30, H=64, E=4, k=4, F=64, c=8, K_max=8),
 }
 
 
