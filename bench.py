@@ -301,7 +301,7 @@ def graph_replay(torch, args, call, outs, units):
     return {"ms_per_step": round(ms, 4), "per_s": round(units / (ms / 1e3), 1)}
 
 
-def blas_yardstick(torch, wl, plan, stages):
+def blas_yardstick(torch, wl, plan, stages, backward=False):
     """torch.bmm (the vendor BLAS) on one chunk's expert products with every
     expert given the same number of rows, stored contiguously: E x [m, H] x
     [H, 2F] for gate and up side by side, E x [m, F] x [F, H] for the down
@@ -318,19 +318,21 @@ def blas_yardstick(torch, wl, plan, stages):
     Hh = torch.randn(E, m, F, device=dev, dtype=bf, generator=g)
     Wd = torch.randn(E, F, H, device=dev, dtype=bf, generator=g)
     res = {"rows_per_expert": m}
-    for name, fn, flops in (("gemm_up", lambda: torch.bmm(A, Wgu), 4.0 * E * m * H * F),
-                            ("gemm_down", lambda: torch.bmm(Hh, Wd), 2.0 * E * m * H * F)):
+    def time_us(fn, reps=20):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 20
         e0.record()
         for _ in range(reps):
             fn()
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    for name, fn, flops in (("gemm_up", lambda: torch.bmm(A, Wgu), 4.0 * E * m * H * F),
+                            ("gemm_down", lambda: torch.bmm(Hh, Wd), 2.0 * E * m * H * F)):
+        us = time_us(fn)
         ours = stages[name]
         res[name] = {"bmm_us": round(us, 2), "bmm_TFLOP_per_s": round(flops / us / 1e6, 1),
                      "grouped_us": ours["us_per_launch"],
@@ -338,6 +340,22 @@ def blas_yardstick(torch, wl, plan, stages):
         log(f"  yardstick {name}: torch.bmm {us:.1f} us ({flops / us / 1e6:.0f} TFLOP/s) on "
             f"{E} x [{m} rows]; grouped GEMM {ours['us_per_launch']} us")
     del A, Wgu, Hh, Wd
+    if backward:
+        # the weight-gradient shapes (K = the m rows of an expert), bf16
+        # outputs: the library has no fp32 read-modify-write of dW, which the
+        # layer's weight-gradient GEMMs also do (4x these output bytes)
+        XT = torch.randn(E, H, m, device=dev, dtype=bf, generator=g)
+        D = torch.randn(E, m, 2 * F, device=dev, dtype=bf, generator=g)
+        HT = torch.randn(E, F, m, device=dev, dtype=bf, generator=g)
+        DY = torch.randn(E, m, H, device=dev, dtype=bf, generator=g)
+        o1 = torch.empty(E, H, 2 * F, device=dev, dtype=bf)
+        o2 = torch.empty(E, F, H, device=dev, dtype=bf)
+        for name, fn, flops in (("wgrad_gate_up", lambda: torch.bmm(XT, D, out=o1), 4.0 * E * m * H * F),
+                                ("wgrad_down", lambda: torch.bmm(HT, DY, out=o2), 2.0 * E * m * H * F)):
+            us = time_us(fn)
+            res[name] = {"bmm_us": round(us, 2), "bmm_TFLOP_per_s": round(flops / us / 1e6, 1)}
+            log(f"  yardstick {name}: torch.bmm {us:.1f} us ({flops / us / 1e6:.0f} TFLOP/s), bf16 out")
+        del XT, D, HT, DY, o1, o2
     return res
 
 
@@ -524,7 +542,8 @@ def main():
                      for s in ("gemm_up", "gemm_down"))
     gemm_us = sum(stages[s]["us_per_launch"] * K for s in ("gemm_up", "gemm_down"))
 
-    yard = blas_yardstick(torch, wl, plan, stages) if args.blas_yardstick and bf else None
+    yard = (blas_yardstick(torch, wl, plan, stages, args.backward)
+            if args.blas_yardstick and bf else None)
 
     fb = None
     if args.backward:
