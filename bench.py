@@ -133,12 +133,7 @@ def cce_main(args, datagen, np, torch, B):
     dW = torch.empty((V, H), dtype=torch.float32, device=dev)
     # a plain 256 MiB device copy, outside the timed region: the reference for
     # scaling the HBM byte counters of a profiled run
-    cp_src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
-    cp_dst = torch.empty_like(cp_src)
-    cp_dst.copy_(cp_src)
-    torch.cuda.synchronize()
-    del cp_src, cp_dst
-    torch.cuda.empty_cache()
+    hbm_copy = calibration_copy(torch, dev)
     torch.cuda.synchronize()
     mem0 = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
@@ -235,6 +230,7 @@ def cce_main(args, datagen, np, torch, B):
         "forward_ms": round(ms_f, 4),
         "gemm_TFLOP_per_s": round(gemm_flops / (ms / 1e3) / 1e12, 1),
         "roofline": roof,
+        "hbm_copy": hbm_copy,
         "memory": {"strip_bound_bytes": plan.strip_bound_bytes,
                    "unchunked_logit_bytes": plan.unchunked_logit_bytes,
                    "fwd_workspace_bytes": plan.fwd_workspace_bytes,
@@ -262,6 +258,29 @@ def cce_main(args, datagen, np, torch, B):
                                          f"loss, dX and dW, {cpu_s:.1f} s"}
         log(f"cpu baseline: {cpu_s:.2f} s, {threads} BLAS threads")
     print(json.dumps(out), flush=True)
+
+
+def calibration_copy(torch, dev):
+    """A 256 MiB device-to-device copy (read 256 MiB, write 256 MiB).  The
+    first one is the reference for scaling a profiled run's HBM byte
+    counters; five more are timed for the rate a plain copy reaches on this
+    machine (context for the HBM roofline, whose peak stays the published
+    8 TB/s)."""
+    src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * 2 * src.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"plain 256 MiB copy: {gbs:.0f} GB/s (read + write)")
+    return {"GB_per_s": round(gbs, 1), "bytes_per_copy": 2 * (256 << 20)}
 
 
 def graph_replay(torch, args, call, outs, units):
@@ -427,12 +446,7 @@ def main():
     # a plain 256 MiB device copy, outside the timed region: the reference
     # for scaling the HBM byte counters of a profiled run (read 256 MiB,
     # write 256 MiB)
-    cp_src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
-    cp_dst = torch.empty_like(cp_src)
-    cp_dst.copy_(cp_src)
-    torch.cuda.synchronize()
-    del cp_src, cp_dst
-    torch.cuda.empty_cache()
+    hbm_copy = calibration_copy(torch, dev)
     # device memory the layer adds on top of its inputs and outputs: the
     # workspace (routing plan + the bounded per-chunk buffers)
     mem0 = torch.cuda.memory_allocated(dev)
@@ -613,6 +627,7 @@ def main():
                    "parallelism": "single GPU"},
         "forward_backward": fb,
         "graph_replay": graph,
+        "hbm_copy": hbm_copy,
         "blas_yardstick": yard,
         "roofline": roof,
         "grouped_gemm": {"TFLOP_per_s": round(gemm_flops / gemm_us / 1e6, 1),
