@@ -11,6 +11,8 @@ through the C ABI, against the full fp64 oracle (forward and backward):
   * every token routed to the same two experts (a Zipf(12) router bias over
     8 experts with top-2): two full segments per chunk, six empty experts;
   * the largest k: k = E = 64, every token in every expert;
+  * the largest E: 1024 experts with top-64 (most experts hold a few rows
+    of a chunk, many none);
   * fp32 with k = E = 4;
   * N = 0: both entry points succeed and enqueue nothing but the weight
     gradients' zero fill.
@@ -52,6 +54,9 @@ CASES = {
                                      c=300, K_max=4, zipf_s=12.0),
     # k = E = 64
     "k64_bf16": BF.with_(name="k64_bf16", N=10, H=64, E=64, k=64, F=64, c=4, K_max=4),
+    # E = 1024 (the largest the ABI takes), top-64: 2 chunks of 100 tokens
+    "max_experts_bf16": BF.with_(name="max_experts_bf16", N=200, H=64, E=1024, k=64, F=64, c=100,
+                                 K_max=4),
     # fp32, k = E = 4
     "k_eq_E_f32": F32.with_(name="k_eq_E_f32", N=30, H=64, E=4, k=4, F=64, c=8, K_max=8),
 }
