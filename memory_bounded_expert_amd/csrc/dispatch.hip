@@ -1,5 +1,6 @@
-// Data movement around the grouped GEMMs: gather (permute), gate-weighted
-// combine (unpermute), and the backward pass's elementwise and combine steps
+// Data movement around the grouped GEMMs: gather (permute), combine
+// (unpermute: the sum of a token's gate-scaled expert rows), and the backward
+// pass's elementwise and combine steps
 // ("Training Trillion-Parameter MoE ...", section 3.3: Permute, Grouped GEMM,
 // Unpermute; "Memory-Efficient Expert Routing ...", section 2.1: outputs are
 // returned and recombined).
