@@ -509,6 +509,16 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
           for (int j = 0; j < FN; ++j) Mfma<bf16_t>::run(fa[set][ks][i], fb[set][ks][g][j], acc[g][i][j]);
   };
 
+  // Row scales of a scaled store, one per lane (the wave's row slice is at
+  // most 64 rows): requested before the pipeline's first loads, so they
+  // have landed long before the epilogue reads them
+  float row_scale_lane = 1.f;
+  if constexpr (MODE == Mode::Rows && EPI == Epi::Store) {
+    static_assert(WM <= 64, "one row scale per lane");
+    const int row = m0 + wm * WM + lane;
+    if (p.row_scale && lane < WM && row < row_end) row_scale_lane = p.row_scale[row];
+  }
+
   // ---- pipeline.  NS stages; tile t goes to stage t % NS.  The prologue
   // fills every stage and reads tile 0's fragments.  Iteration kt then
   //   waits until tile kt+1 has landed (this thread's loads, then everyone's,
@@ -521,16 +531,6 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   // of the final iteration hits such a copy and is not used.  The loop is
   // unrolled so that every stage index and register set is a compile-time
   // constant.
-  // Row scales of a scaled store, one per lane (the wave's row slice is at
-  // most 64 rows): requested before the pipeline's first loads, so they
-  // have landed long before the epilogue reads them
-  float row_scale_lane = 1.f;
-  if constexpr (MODE == Mode::Rows && EPI == Epi::Store) {
-    static_assert(WM <= 64, "one row scale per lane");
-    const int row = m0 + wm * WM + lane;
-    if (p.row_scale && lane < WM && row < row_end) row_scale_lane = p.row_scale[row];
-  }
-
   constexpr int U = (NS % 2 == 0) ? NS : 2 * NS;
   if (nk > 0) {  // (an expert with no rows in store mode skips to the epilogue)
   const int last = nk - 1;
