@@ -248,7 +248,7 @@ MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const voi
       MOE_CHECK(gemm_up_swiglu(P.dtype, rgl, X, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st,
                                perm_i, P.k, P.N, gs));
     } else {
-      MOE_CHECK(launch_gather(P.dtype, X, xp, perm_i, R, P.k, P.N, P.H, st));
+      MOE_CHECK(launch_gather(P.dtype, X, xp, topk_idx, pb.pos, P.E, P.K, i, g.n, P.k, P.H, st));
       MOE_CHECK(gemm_up_swiglu(P.dtype, rgl, xp, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st,
                                nullptr, 1, 0, gs));
     }
@@ -315,10 +315,10 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
     const RowsGeom rg = rows_geom(pb, P, i, R);
     const int32_t* perm_i = pb.perm + g.pair_base;
     // recompute this chunk's expert intermediates
-    MOE_CHECK(launch_gather(P.dtype, X, xp, perm_i, R, P.k, P.N, P.H, st));
+    MOE_CHECK(launch_gather(P.dtype, X, xp, topk_idx, pb.pos, P.E, P.K, i, g.n, P.k, P.H, st));
     MOE_CHECK(gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, a, u, P.H, P.F, st));
     // backward through the chunk
-    MOE_CHECK(launch_gather(P.dtype, dY, o, perm_i, R, P.k, P.N, P.H, st));
+    MOE_CHECK(launch_gather(P.dtype, dY, o, topk_idx, pb.pos, P.E, P.K, i, g.n, P.k, P.H, st));
     if (fused_swiglu) {
       MOE_CHECK(gemm_dh_swiglu(rg, o, W_down, a, u, h, perm_i, gates, dgp, (int64_t)P.k * P.c_eff,
                                P.N * P.k, P.H, P.F, st));
@@ -413,7 +413,7 @@ MOE_API int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk
     const RowsGeom* gs = split ? &rgs : nullptr;
     switch (stage) {
       case MOE_STAGE_GATHER:
-        err = launch_gather(P.dtype, X, xp, perm_i, R, P.k, P.N, P.H, st);
+        err = launch_gather(P.dtype, X, xp, topk_idx, pb.pos, P.E, P.K, chunk, g.n, P.k, P.H, st);
         break;
       case MOE_STAGE_GEMM_UP:
         err = fused ? gemm_up_swiglu(P.dtype, rgl, X, W_gate, W_up, h, nullptr, nullptr, P.H,

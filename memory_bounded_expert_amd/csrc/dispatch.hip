@@ -20,21 +20,32 @@ inline unsigned grid_for(int64_t work, int64_t per_block) {
   return (unsigned)(g < 1 ? 1 : g);
 }
 
-// Xp[r] = src[t(r)], t(r) = perm[r] / k.
+// dst[pos[t, s]] = src[t] for the tokens t = i + j K of chunk i and their k
+// slots: each token's row is read once and written to its k rows of the
+// chunk's expert-contiguous buffer (every row of the buffer holds exactly one
+// pair).  Slots whose expert index is out of range (a corrupt routing input)
+// have no row and are skipped.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ src,
                                                           T* __restrict__ dst,
-                                                          const int32_t* __restrict__ perm,
-                                                          int64_t R, int k, int64_t N, int H) {
+                                                          const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ pos,
+                                                          int E, int K, int i, int64_t n_i,
+                                                          int64_t R, int k, int H) {
   const int cpr = H * (int)sizeof(T) / 16;
-  const int64_t total = R * cpr;
+  const int64_t total = n_i * cpr;
   for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < total;
        q += (int64_t)gridDim.x * kThreads) {
-    const int64_t r = q / cpr;
-    const int c = (int)(q - r * cpr);
-    int64_t t = perm[r] / k;
-    if ((uint64_t)t >= (uint64_t)N) t = 0;  // only on a corrupt plan: stay in bounds
-    reinterpret_cast<u32x4_t*>(dst + r * H)[c] = reinterpret_cast<const u32x4_t*>(src + t * H)[c];
+    const int64_t j = q / cpr;
+    const int c = (int)(q - j * cpr);
+    const int64_t t = i + j * (int64_t)K;
+    const u32x4_t v = reinterpret_cast<const u32x4_t*>(src + t * H)[c];
+    for (int s = 0; s < k; ++s) {
+      const int e = idx[t * k + s];
+      const int64_t r = pos[t * k + s];
+      if ((unsigned)e < (unsigned)E && (uint64_t)r < (uint64_t)R)
+        reinterpret_cast<u32x4_t*>(dst + r * H)[c] = v;
+    }
   }
 }
 
@@ -306,17 +317,19 @@ __global__ __launch_bounds__(kThreads) void dwr_kernel(const T* __restrict__ Xp,
 
 }  // namespace
 
-hipError_t launch_gather(int dtype, const void* src, void* dst, const int32_t* perm, int64_t R,
-                         int k, int64_t N, int H, hipStream_t st) {
-  if (R == 0) return hipSuccess;
-  const int64_t chunks = R * H * elem_bytes(dtype) / 16;
-  const unsigned grid = grid_for(chunks, kThreads * 4);
+hipError_t launch_gather(int dtype, const void* src, void* dst, const int32_t* idx,
+                         const int32_t* pos, int E, int K, int i, int64_t n_i, int k, int H,
+                         hipStream_t st) {
+  if (n_i == 0) return hipSuccess;
+  const int64_t chunks = n_i * H * elem_bytes(dtype) / 16;
+  const unsigned grid = grid_for(chunks, kThreads);
+  const int64_t R = n_i * k;
   if (dtype == MOE_BF16)
-    gather_kernel<bf16_t><<<grid, kThreads, 0, st>>>((const bf16_t*)src, (bf16_t*)dst, perm, R, k,
-                                                     N, H);
+    gather_kernel<bf16_t><<<grid, kThreads, 0, st>>>((const bf16_t*)src, (bf16_t*)dst, idx, pos, E,
+                                                     K, i, n_i, R, k, H);
   else
-    gather_kernel<float><<<grid, kThreads, 0, st>>>((const float*)src, (float*)dst, perm, R, k, N,
-                                                    H);
+    gather_kernel<float><<<grid, kThreads, 0, st>>>((const float*)src, (float*)dst, idx, pos, E, K,
+                                                    i, n_i, R, k, H);
   return hipGetLastError();
 }
 

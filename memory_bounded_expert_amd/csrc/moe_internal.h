@@ -150,8 +150,11 @@ hipError_t launch_plan(const int32_t* idx, int64_t N, int K, int k, int E, const
                        hipStream_t st, const float* gates = nullptr);
 
 // Data movement (dtype-dispatched: 0 f32, 1 bf16).
-hipError_t launch_gather(int dtype, const void* src, void* dst, const int32_t* perm_chunk, int64_t R,
-                         int k, int64_t N, int H, hipStream_t st);
+// Permute (gather) of chunk i: dst[pos[t, s]] = src[t] for each token t of the
+// chunk and slot s with a valid expert idx[t, s] (each token row read once).
+hipError_t launch_gather(int dtype, const void* src, void* dst, const int32_t* idx,
+                         const int32_t* pos, int E, int K, int i, int64_t n_i, int k, int H,
+                         hipStream_t st);
 // Y[t] = sum_s O[pos[t, s]] over the k gate-scaled expert rows of each token
 // of chunk i.
 hipError_t launch_combine(int dtype, const void* O, const int32_t* pos, void* Y, int64_t N, int K,
