@@ -334,7 +334,7 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
                                  P.K, i, g.n, P.k, P.E, P.H, st, fused_swiglu ? dgp : nullptr,
                                  fused_swiglu ? dh_ntiles(rg, P.F) : 0, (int64_t)P.k * P.c_eff));
     if (dW_r)
-      MOE_CHECK(launch_dwr(P.dtype, xp, perm_i, rg.offsets, dlogits, dW_r, P.k, P.E, P.H, P.N, st));
+      MOE_CHECK(launch_dwr(P.dtype, X, perm_i, rg.offsets, dlogits, dW_r, P.k, P.E, P.H, P.N, st));
   }
   fill_stats(stats, P, launches, L.total,
              (size_t)P.k * P.c_eff * P.F * (3 * elem_bytes(P.dtype) + (fused_swiglu ? 0 : 4)));

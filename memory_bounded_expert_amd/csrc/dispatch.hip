@@ -257,14 +257,16 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void dwr_kernel(const T* __restrict__ Xp,
+__global__ __launch_bounds__(kThreads) void dwr_kernel(const T* __restrict__ X,
                                                        const int32_t* __restrict__ perm,
                                                        const int32_t* __restrict__ offsets,
                                                        const float* __restrict__ dlogits,
                                                        float* __restrict__ dWr, int k, int E,
                                                        int H, int64_t N) {
   // dW_r[:, e] += sum over the chunk's rows r of expert e of
-  // Xp[r, :] * dlogits[t(r), e]; rows of other experts would add
+  // X[t(r), :] * dlogits[t(r), e], t(r) = perm[r] / k (the token's row of X
+  // itself: each token is read by its k experts' work-groups, from cache
+  // after the first); rows of other experts would add
   // dlogits[t, e] = 0 exactly, so they are skipped.  One work-group per
   // (64-wide column block of H, expert): CPB threads cover a row's 64 values
   // with 16-byte loads and RG row groups stride the expert's segment (rows
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void dwr_kernel(const T* __restrict__ Xp,
   auto row = [&](int r, float& d, float* v) __attribute__((always_inline)) {
     const int64_t t = perm[r] / k;
     d = (uint64_t)t < (uint64_t)N ? dlogits[t * E + e] : 0.f;  // t >= N only on a corrupt plan
-    unpack16(*reinterpret_cast<const u32x4_t*>(Xp + (int64_t)r * H + col), v, T());
+    unpack16(*reinterpret_cast<const u32x4_t*>(X + ((uint64_t)t < (uint64_t)N ? t : 0) * H + col), v, T());
   };
   int r = r0 + rg;
   for (; r + 3 * RG < r1; r += 4 * RG) {
@@ -404,16 +406,16 @@ hipError_t launch_combine_bwd(int dtype, const void* dXp, const void* WrT, const
   return hipGetLastError();
 }
 
-hipError_t launch_dwr(int dtype, const void* Xp, const int32_t* perm, const int32_t* offsets,
+hipError_t launch_dwr(int dtype, const void* X, const int32_t* perm, const int32_t* offsets,
                       const float* dlogits, float* dWr, int k, int E, int H, int64_t N,
                       hipStream_t st) {
   // H is a multiple of 64 (checked when the plan is made)
   const dim3 grid((unsigned)(H / 64), (unsigned)E);
   if (dtype == MOE_BF16)
-    dwr_kernel<bf16_t><<<grid, kThreads, 0, st>>>((const bf16_t*)Xp, perm, offsets, dlogits, dWr, k,
+    dwr_kernel<bf16_t><<<grid, kThreads, 0, st>>>((const bf16_t*)X, perm, offsets, dlogits, dWr, k,
                                                   E, H, N);
   else
-    dwr_kernel<float><<<grid, kThreads, 0, st>>>((const float*)Xp, perm, offsets, dlogits, dWr, k,
+    dwr_kernel<float><<<grid, kThreads, 0, st>>>((const float*)X, perm, offsets, dlogits, dWr, k,
                                                  E, H, N);
   return hipGetLastError();
 }

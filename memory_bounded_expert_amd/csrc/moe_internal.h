@@ -172,7 +172,9 @@ hipError_t launch_combine_bwd(int dtype, const void* dXp, const void* WrT, const
                               void* dX, float* dlogits, int64_t N, int K, int i, int64_t n_i,
                               int k, int E, int H, hipStream_t st, const float* dgp = nullptr,
                               int nparts = 0, int64_t prow = 0);
-hipError_t launch_dwr(int dtype, const void* Xp, const int32_t* perm_chunk, const int32_t* offsets,
+// dW_r += X^T dlogits over chunk i's pairs (row r of the chunk's buffer is token
+// perm_chunk[r] / k of X), summed per expert in row order.
+hipError_t launch_dwr(int dtype, const void* X, const int32_t* perm_chunk, const int32_t* offsets,
                       const float* dlogits, float* dWr, int k, int E, int H, int64_t N,
                       hipStream_t st);
 
