@@ -197,16 +197,18 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
   constexpr int EPC = Elem<T>::kPer16B;
   __shared__ float dl[64];
   __shared__ float dgs[64];
+  __shared__ float gs[64];
   __shared__ int ex[64];
   __shared__ int64_t rows[64];
   const int cpr = H / EPC;
   for (int64_t j = blockIdx.x; j < n_i; j += gridDim.x) {
     const int64_t t = i + j * (int64_t)K;
     if ((int)threadIdx.x < k) {
+      // slot s's loads in parallel; thread 0 then works from LDS only
       const int s = threadIdx.x;
+      const int64_t r = pos[t * k + s];
       float v;
       if (dgp) {
-        const int64_t r = pos[t * k + s];
         v = 0.f;
         for (int nt = 0; nt < nparts; ++nt) v += dgp[nt * prow + r];
         dgates[t * k + s] = v;
@@ -214,18 +216,16 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
         v = dgates[t * k + s];
       }
       dgs[s] = v;
+      gs[s] = gates[t * k + s];
+      const int e = idx[t * k + s];
+      ex[s] = ((unsigned)e < (unsigned)E) ? e : 0;
+      rows[s] = r;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
       float sdot = 0.f;
-      for (int s = 0; s < k; ++s) sdot = fmaf(gates[t * k + s], dgs[s], sdot);
-      for (int s = 0; s < k; ++s) {
-        const float g = gates[t * k + s];
-        dl[s] = g * (dgs[s] - sdot);
-        int e = idx[t * k + s];
-        ex[s] = ((unsigned)e < (unsigned)E) ? e : 0;
-        rows[s] = pos[t * k + s];
-      }
+      for (int s = 0; s < k; ++s) sdot = fmaf(gs[s], dgs[s], sdot);
+      for (int s = 0; s < k; ++s) dl[s] = gs[s] * (dgs[s] - sdot);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kThreads) {
