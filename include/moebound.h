@@ -30,9 +30,10 @@
  * at most k*c_eff rows, run through the experts and combined back, so the
  * top-k-expanded buffer of the whole batch never exists.  The H-wide
  * dispatch buffers take at most 2*k*c_eff*H*b bytes ([BSO] "Memory bound"
- * with E_p = 1 and c read as c_eff); the bf16 forward needs only half of
- * that, because its gate/up GEMM reads each permuted input row straight from
- * X.  The result does not depend on K: per-token
+ * with E_p = 1 and c read as c_eff); bf16 needs only half of that, because
+ * its forward and backward read each permuted input row straight from X
+ * (when X fits 32-bit buffer offsets, and in the backward N*k*k < 2^32).
+ * The result does not depend on K: per-token
  * outputs are bitwise identical for every (c, K_max).
  *
  * Conventions for every entry point:
@@ -96,9 +97,9 @@ typedef struct moe_stats {
     int64_t c_eff;
     int64_t max_pairs_per_chunk; /* largest R_i = k * n_i over the chunks     */
     int64_t dispatch_bytes;      /* H-wide per-chunk dispatch buffers carved:
-                                    k*c_eff*H*b each; one in the bf16 forward
-                                    (expert outputs; inputs read from X in
-                                    place), two otherwise                     */
+                                    k*c_eff*H*b each; one in bf16 (expert
+                                    outputs, or dY rows then dXp; inputs read
+                                    from X in place), two otherwise           */
     int64_t dispatch_bound_bytes;/* 2 * k * c_eff * H * b                     */
     int64_t intermediate_bytes;  /* F-wide per-chunk intermediates            */
     int64_t workspace_bytes;     /* workspace bytes the call used             */

@@ -55,8 +55,9 @@ Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_d
     L.pos = take(N * k * 4);
     if (pass == Pass::Forward) L.row_gates = take(N * k * 4);
     const size_t rows = k * ce;
-    // the bf16 forward reads its permuted inputs straight from X
-    if (pass == Pass::Backward || !fused_gather(p)) L.xp = take(rows * H * b);
+    // the bf16 passes read their permuted inputs straight from X
+    if (pass == Pass::Backward ? !fused_gather_bwd(p) : !fused_gather(p))
+      L.xp = take(rows * H * b);
     L.o = take(rows * H * b);
     L.h = take(rows * F * b);
     if (pass == Pass::Backward) {
@@ -309,14 +310,22 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
   float* dh = (float*)(ws + L.dh);
   float* dgp = (float*)(ws + L.dgp);
   const bool fused_swiglu = P.dtype == MOE_BF16;
+  // bf16: the recompute and the gate/up weight gradient read the chunk's
+  // permuted input rows from X through perm (no gather, no Xp)
+  const bool fused = fused_gather_bwd(P);
   for (int i = 0; i < P.K; ++i) {
     const ChunkGeom g = chunk_geom(P.N, P.K, P.k, i);
     const int64_t R = (int64_t)P.k * g.n;
     const RowsGeom rg = rows_geom(pb, P, i, R);
     const int32_t* perm_i = pb.perm + g.pair_base;
     // recompute this chunk's expert intermediates
-    MOE_CHECK(launch_gather(P.dtype, X, xp, topk_idx, pb.pos, P.E, P.K, i, g.n, P.k, P.H, st));
-    MOE_CHECK(gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, a, u, P.H, P.F, st));
+    if (fused) {
+      MOE_CHECK(gemm_up_swiglu(P.dtype, rg, X, W_gate, W_up, h, a, u, P.H, P.F, st, perm_i, P.k,
+                               P.N));
+    } else {
+      MOE_CHECK(launch_gather(P.dtype, X, xp, topk_idx, pb.pos, P.E, P.K, i, g.n, P.k, P.H, st));
+      MOE_CHECK(gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, a, u, P.H, P.F, st));
+    }
     // backward through the chunk
     MOE_CHECK(launch_gather(P.dtype, dY, o, topk_idx, pb.pos, P.E, P.K, i, g.n, P.k, P.H, st));
     if (fused_swiglu) {
@@ -327,8 +336,8 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
       MOE_CHECK(launch_swiglu_bwd(P.dtype, dh, a, u, h, perm_i, gates, dg, R, P.F, P.N * P.k, st));
     }
     MOE_CHECK(gemm_wgrad_d(P.dtype, rg.offsets, h, o, dW_down, P.E, P.H, P.F, st, wg_init && i == 0));
-    MOE_CHECK(gemm_wgrad_gu(P.dtype, rg.offsets, xp, a, u, dW_gate, dW_up, P.E, P.H, P.F, st,
-                            wg_init && i == 0));
+    MOE_CHECK(gemm_wgrad_gu(P.dtype, rg.offsets, fused ? X : xp, a, u, dW_gate, dW_up, P.E, P.H,
+                            P.F, st, wg_init && i == 0, fused ? perm_i : nullptr, P.k, P.N));
     MOE_CHECK(gemm_dx(P.dtype, rg, a, u, W_gate, W_up, o, P.H, P.F, st));
     MOE_CHECK(launch_combine_bwd(P.dtype, o, wrt, topk_idx, pb.pos, gates, dg, dX, dlogits, P.N,
                                  P.K, i, g.n, P.k, P.E, P.H, st, fused_swiglu ? dgp : nullptr,
@@ -337,7 +346,8 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
       MOE_CHECK(launch_dwr(P.dtype, X, perm_i, rg.offsets, dlogits, dW_r, P.k, P.E, P.H, P.N, st));
   }
   fill_stats(stats, P, launches, L.total,
-             (size_t)P.k * P.c_eff * P.F * (3 * elem_bytes(P.dtype) + (fused_swiglu ? 0 : 4)));
+             (size_t)P.k * P.c_eff * P.F * (3 * elem_bytes(P.dtype) + (fused_swiglu ? 0 : 4)),
+             fused ? 1 : 2);
   return MOE_OK;
 }
 

@@ -45,10 +45,10 @@ hipError_t dx_bf16(const Params& p, dim3 grid, int bn, int rt, hipStream_t st) {
   return launch_lds<Mode::Rows, Shape<128, 64, 2, 4, 64, 1>, false, true, true, true, Epi::Store>(p, grid, st);
 }
 
-template <int BM>
+template <int BM, Mode MODE>
 hipError_t wgu_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
-  if (bn == 128) return launch_lds<Mode::Expert, Shape<BM, 128, 2, 2, 32, 2>, true, false, false, false, Epi::AccF32>(p, grid, st);
-  return launch_lds<Mode::Expert, Shape<BM, 64, 2, 4, 64, 1>, true, false, false, false, Epi::AccF32>(p, grid, st);
+  if (bn == 128) return launch_lds<MODE, Shape<BM, 128, 2, 2, 32, 2>, true, false, false, false, Epi::AccF32>(p, grid, st);
+  return launch_lds<MODE, Shape<BM, 64, 2, 4, 64, 1>, true, false, false, false, Epi::AccF32>(p, grid, st);
 }
 
 template <int BM>
@@ -139,11 +139,20 @@ hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du,
 
 hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, const void* da,
                          const void* du, float* dWg, float* dWu, int E, int H, int F,
-                         hipStream_t st, bool init) {
+                         hipStream_t st, bool init, const int32_t* rows, int k, int64_t x_rows) {
   if (init && dtype != MOE_BF16) return hipErrorInvalidValue;
   Params p{};
   p.acc_init = init ? 1 : 0;
   p.A = Xp; p.lda = H;
+  if (rows) {
+    // K-row r is row rows[r] / k of X: the division as a multiply-shift,
+    // exact while every rows[r] * k < 2^32 (rows[r] < x_rows * k)
+    if (dtype != MOE_BF16 || k < 1 || x_rows < 1 || !indexed_rows_ok(x_rows, k))
+      return hipErrorInvalidValue;
+    p.k_rows = rows;
+    p.k_row_mul = ((1ull << 32) + (uint64_t)k - 1) / (uint64_t)k;
+    p.k_src_rows = x_rows;
+  }
   p.B = da; p.B2 = du; p.ldb = F;
   p.C = dWg; p.C2 = dWu; p.ldc = F; p.c_estride = (int64_t)H * F;
   p.M = H; p.N = F;
@@ -151,8 +160,12 @@ hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, cons
   const int bm = H % 128 == 0 ? 128 : 64;
   const int bn = F % 128 == 0 ? 128 : 64;
   const dim3 grid((unsigned)(H / bm), (unsigned)(F / bn), (unsigned)E);
+  if (rows)
+    return bm == 128 ? wgu_bf16<128, Mode::ExpertIdx>(p, grid, bn, st)
+                     : wgu_bf16<64, Mode::ExpertIdx>(p, grid, bn, st);
   if (dtype == MOE_BF16)
-    return bm == 128 ? wgu_bf16<128>(p, grid, bn, st) : wgu_bf16<64>(p, grid, bn, st);
+    return bm == 128 ? wgu_bf16<128, Mode::Expert>(p, grid, bn, st)
+                     : wgu_bf16<64, Mode::Expert>(p, grid, bn, st);
   return bm == 128 ? wgu_t<float, 128>(p, grid, bn, st) : wgu_t<float, 64>(p, grid, bn, st);
 }
 

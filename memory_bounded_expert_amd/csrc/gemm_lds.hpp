@@ -79,6 +79,17 @@ __device__ __forceinline__ void lds_load16(const i32x4_t& srd, void* lds, uint32
                : "memory", "m0");
 }
 
+// 4 bytes per lane from a buffer straight into LDS at lds + 4 * lane (every
+// lane writes, lanes past the resource write zeros)
+__device__ __forceinline__ void lds_load4(const i32x4_t& srd, void* lds, uint32_t voff) {
+  const uint32_t m0v =
+      __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_void_p)lds));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(srd)
+               : "memory", "m0");
+}
+
 // Work-group barrier for the LDS pipeline: waits for this wave's LDS reads
 // only (outstanding global->LDS loads stay in flight across it).  The wait is
 // the builtin, not inline asm, so that the compiler's own wait-count tracking
@@ -131,7 +142,9 @@ struct Shape {
   static constexpr int WG_PER_CU = WG_PER_CU_;
 };
 
-template <class S, bool DUAL>
+// KIDX: room for the row-indexed K slots (at most 6 stages of 256 bytes per
+// wave) comes off the stages' budget
+template <class S, bool DUAL, bool KIDX = false>
 struct LdsCfg {
   static constexpr int BM = S::BM, BN = S::BN, BK = S::BK;
   static constexpr int NB = DUAL ? 2 : 1;
@@ -140,7 +153,7 @@ struct LdsCfg {
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = NCOL * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int BUDGET = kLdsBytes / S::WG_PER_CU;
+  static constexpr int BUDGET = kLdsBytes / S::WG_PER_CU - (KIDX ? S::WGM * S::WGN * 6 * 256 : 0);
   static constexpr int NS_FIT = (BUDGET / STAGE) > 6 ? 6 : (BUDGET / STAGE);
   // an even stage count keeps the unrolled main loop at NS steps (the two
   // fragment register sets alternate); odd counts above 3 drop one stage
@@ -187,12 +200,31 @@ __device__ __forceinline__ int kswz(int r) {
   else return (r >> 2) & 3;
 }
 
+// Row-indexed K (Mode::ExpertIdx): K-rows per wave per K-tile (a wave's A
+// loads of an M-contiguous tile cover BK / WAVES consecutive rows), and the
+// slots' place and size in LDS (past the stages; per wave, one 256-byte slot
+// per stage, since a dword load into LDS writes all 64 lanes).
+template <int BK, int WAVES>
+constexpr int kidx_rows() {
+  static_assert(BK % WAVES == 0 && BK / WAVES <= 64, "index rows per wave");
+  return BK / WAVES;
+}
+template <class C>
+constexpr int kidx_offset() { return C::NS * C::STAGE; }
+template <Mode MODE, class S, bool DUAL>
+constexpr int lds_bytes() {
+  using C = LdsCfg<S, DUAL, MODE == Mode::ExpertIdx>;
+  constexpr int b = C::NS * C::STAGE + (MODE == Mode::ExpertIdx ? C::WAVES * C::NS * 256 : 0);
+  static_assert(b <= kLdsBytes / S::WG_PER_CU, "LDS over the work-group's share");
+  return b;
+}
+
 // The work-group's whole product.  bid is the work-group's index in a Rows
 // grid (a pair launch offsets the second product's ids); the other modes
 // read blockIdx themselves.
 template <Mode MODE, class S, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
 __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
-  using C = LdsCfg<S, DUAL>;
+  using C = LdsCfg<S, DUAL, MODE == Mode::ExpertIdx>;
   using T = bf16_t;
   constexpr int BM = S::BM, BN = S::BN, BK = S::BK, NB = C::NB, NS = C::NS, CK = C::CK;
   constexpr int WM = BM / S::WGM, WN = BN / S::WGN;
@@ -204,6 +236,11 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   static_assert(!(DUAL && KCAT), "DUAL and KCAT are exclusive");
   static_assert(!(DUAL && B_K), "DUAL needs an N-contiguous B");
   static_assert(A_K || RCA >= 8, "M-contiguous A needs BM >= 64");
+  constexpr bool EXPERT = MODE == Mode::Expert || MODE == Mode::ExpertIdx;
+  constexpr bool KIDX = MODE == Mode::ExpertIdx;
+  static_assert(!KIDX || (!A_K && !KCAT), "row-indexed K needs an M-contiguous A");
+  // loads per thread per K-tile (an indexed product adds its index block)
+  constexpr int PT = C::PER_TILE + (KIDX ? 1 : 0);
   static_assert(B_K || RCB >= 8, "N-contiguous B needs BN >= 64");
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -289,6 +326,10 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
       }
     }
     rA2 = KCAT ? make_srd(A2p + (int64_t)m0 * p.lda, rows * p.lda * TS) : rA;
+  } else if constexpr (KIDX) {
+    // the whole source matrix from column m0: row offsets come per K-row
+    rA = make_srd(Ap + m0, (p.k_src_rows * p.lda - m0) * TS);
+    rA2 = rA;
   } else {
     rA = make_srd(Ap + k_begin * p.lda + m0, (int64_t)k_len * p.lda * TS);
     rA2 = rA;
@@ -299,8 +340,8 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
     rB = make_srd(Bp + (int64_t)n0 * p.ldb, brows * p.ldb * TS);
     rB2 = KCAT ? make_srd(B2p + (int64_t)n0 * p.ldb, (int64_t)BN * p.ldb * TS) : rB;
   } else {
-    const int64_t rows = (MODE == Mode::Expert) ? (int64_t)k_len : (int64_t)p.K;
-    const int64_t kb = (MODE == Mode::Expert) ? k_begin : 0;
+    const int64_t rows = EXPERT ? (int64_t)k_len : (int64_t)p.K;
+    const int64_t kb = EXPERT ? k_begin : 0;
     rB = make_srd(Bp + kb * p.ldb + n0, (MODE == Mode::Dense ? (int64_t)k_len : rows) * p.ldb * TS);
     rB2 = DUAL ? make_srd(B2p + kb * p.ldb + n0, rows * p.ldb * TS) : rB;
   }
@@ -308,8 +349,31 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   auto stage_a = [&](int s) -> unsigned char* { return smem + s * C::STAGE; };
   auto stage_b = [&](int s) -> unsigned char* { return smem + s * C::STAGE + C::A_BYTES; };
 
-  // ---- issue the loads of K-tile kt into LDS stage s
-  auto issue = [&](int kt, int s) __attribute__((always_inline)) {
+  // ---- row-indexed K (Mode::ExpertIdx).  A wave's A loads of a K-tile cover
+  // KW consecutive K-rows.  Each wave keeps the k_rows entries of
+  // its own rows in private LDS slots past the stages, one 256-byte slot per
+  // stage: the slot of stage s holds the entries of the tile that stage s
+  // receives next.  issue() reads its rows' entries from the slot, then
+  // refills the slot with those of the tile the stage receives NS tiles
+  // later, as one more load of the same K-tile: the pipeline's waits then
+  // also cover the entries (only the wave that loaded a slot reads it).
+  constexpr int KW = kidx_rows<BK, C::WAVES>();
+  i32x4_t rI{};
+  uint32_t ibase = 0;  // this lane's first entry in slot 0 (LDS address)
+  if constexpr (KIDX) {
+    rI = make_srd(p.k_rows + k_begin, (int64_t)k_len * 4);
+    ibase = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_p)smem) + kidx_offset<C>() +
+            (uint32_t)(wave * NS * 256 + (lane / RCA) * 4);
+  }
+  auto load_idx = [&](int kt, int s) __attribute__((always_inline)) {
+    const int r = kt * BK + wave * KW + lane;
+    const uint32_t off = (lane < KW && r < k_len) ? (uint32_t)r * 4u : kOob;
+    lds_load4(rI, smem + kidx_offset<C>() + (wave * NS + s) * 256, off);
+  };
+
+  // ---- issue the loads of K-tile kt into LDS stage s (an indexed product
+  // then loads the k_rows entries of tile kn into the stage's slot)
+  auto issue = [&](int kt, int s, int kn) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     bool second = false;  // K segment of a KCAT product (uniform)
     int kk = k0;
@@ -332,7 +396,18 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
         const int k = ins * RPI + lane / RCA;
         const int c = (lane % RCA) ^ trswz<RCA>(k);
         const int kr = k0 + k;
-        const uint32_t off = kr < k_len ? (uint32_t)((kr * p.lda + c * 8) * TS) : kOob;
+        uint32_t off;
+        if constexpr (KIDX) {
+          // row k of the tile is entry u * RPI + lane / RCA of this wave's slot
+          const int32_t n = *reinterpret_cast<const __attribute__((address_space(3))) int32_t*>(
+              (uintptr_t)(ibase + (uint32_t)(s * 256 + u * RPI * 4)));
+          const uint64_t src = ((uint64_t)(uint32_t)n * p.k_row_mul) >> 32;
+          off = (kr < k_len && src < (uint64_t)p.k_src_rows)
+                    ? (uint32_t)(((int64_t)src * p.lda + c * 8) * TS)
+                    : kOob;
+        } else {
+          off = kr < k_len ? (uint32_t)((kr * p.lda + c * 8) * TS) : kOob;
+        }
         lds_load16(rA, dst, off);
       }
     }
@@ -355,12 +430,13 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
         const int c = (lane % RCB) ^ trswz<RCB>(k);
         const int kr = k0 + k;
         bool ok = true;
-        if constexpr (MODE == Mode::Expert) ok = kr < k_len;
+        if constexpr (EXPERT) ok = kr < k_len;
         if constexpr (MODE == Mode::Dense) ok = n0 + c * 8 < p.N;
         const uint32_t off = ok ? (uint32_t)((kr * p.ldb + c * 8) * TS) : kOob;
         lds_load16((DUAL && g) ? rB2 : rB, dst, off);
       }
     }
+    if constexpr (KIDX) load_idx(kn, s);
   };
 
   // waves wave and wave + 4 share a SIMD; with wm = wave / WGN they cover
@@ -461,6 +537,7 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
     for (int b = 0; b < NBA; ++b) asm volatile("" : "+v"(baseA[b]));
 #pragma unroll
     for (int b = 0; b < NBB; ++b) asm volatile("" : "+v"(baseB[b]));
+    if constexpr (KIDX) asm volatile("" : "+v"(ibase));
   };
   auto ld128 = [](uint32_t addr) __attribute__((always_inline)) -> u32x4_t {
     return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((uintptr_t)addr);
@@ -534,11 +611,17 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   constexpr int U = (NS % 2 == 0) ? NS : 2 * NS;
   if (nk > 0) {  // (an expert with no rows in store mode skips to the epilogue)
   const int last = nk - 1;
+  if constexpr (KIDX) {
+    // the first NS tiles' entries, landed before the prologue reads them
 #pragma unroll
-  for (int s = 0; s < NS; ++s) issue(min(s, last), s);
+    for (int s = 0; s < NS; ++s) load_idx(min(s, last), s);
+    wait_vmcnt<0>();
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) issue(min(s, last), s, min(s + NS, last));
   // a wave whose rows all lie past the segment end only helps with the loads
   const bool active = m0 + wm * WM < row_end;
-  wait_vmcnt<(NS - 1) * C::PER_TILE>();
+  wait_vmcnt<(NS - 1) * PT>();
   lds_barrier();
   if (active) read_frags(0, 0);
   for (int kt0 = 0; kt0 < nk; kt0 += U) {
@@ -546,10 +629,10 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
     for (int u = 0; u < U; ++u) {
       const int kt = kt0 + u;
       if (kt >= nk) break;
-      wait_vmcnt<(NS - 2) * C::PER_TILE>();
+      wait_vmcnt<(NS - 2) * PT>();
       lds_barrier();
       launder();
-      issue(min(kt + NS, last), u % NS);
+      issue(min(kt + NS, last), u % NS, min(kt + 2 * NS, last));
       if (active) {
         read_frags((u + 1) % NS, (u + 1) & 1);
         mfmas(u & 1);
@@ -929,11 +1012,12 @@ hipError_t set_lds_attr(KERN kern, int lds, bool& done) {
 
 template <Mode MODE, class S, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
 hipError_t launch_lds(const Params& p, dim3 grid, hipStream_t st) {
-  using C = LdsCfg<S, DUAL>;
+  using C = LdsCfg<S, DUAL, MODE == Mode::ExpertIdx>;
   auto kern = gemm_lds_kernel<MODE, S, DUAL, A_K, B_K, KCAT, EPI>;
+  constexpr int lds = lds_bytes<MODE, S, DUAL>();
   static bool attr_set = false;
-  if (hipError_t err = set_lds_attr(kern, C::NS * C::STAGE, attr_set); err != hipSuccess) return err;
-  kern<<<grid, C::THREADS, C::NS * C::STAGE, st>>>(p);
+  if (hipError_t err = set_lds_attr(kern, lds, attr_set); err != hipSuccess) return err;
+  kern<<<grid, C::THREADS, lds, st>>>(p);
   return hipGetLastError();
 }
 

@@ -60,6 +60,18 @@ inline bool fused_gather(const moe_plan_t& p) {
   return p.dtype == MOE_BF16 && (int64_t)p.N * p.H * 2 <= 0x7FFFFFF0LL;
 }
 
+// A row index n of a pair (token n / k) divided by a multiply-shift stays
+// exact while n * k < 2^32 for every n < x_rows * k.
+inline bool indexed_rows_ok(int64_t x_rows, int k) {
+  return x_rows >= 0 && k >= 1 && (uint64_t)x_rows * (uint64_t)k * (uint64_t)k < (1ull << 32);
+}
+
+// The bf16 backward also reads the permuted inputs from X (the recompute's
+// gate/up GEMM and the gate/up weight gradient), so it keeps no Xp either.
+inline bool fused_gather_bwd(const moe_plan_t& p) {
+  return fused_gather(p) && indexed_rows_ok(p.N, p.k);
+}
+
 // Upper bound on the row-grouped GEMM's M-tiles of T rows for a chunk of R
 // pairs: sum_e ceil(M_e / T) <= R / T + (number of non-empty experts).
 inline int64_t max_row_tiles(int64_t R, int E, int T) {
@@ -214,10 +226,13 @@ hipError_t gemm_dh_swiglu(const RowsGeom& g, const void* dYp, const void* Wd, vo
 hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du, const void* Wg,
                    const void* Wu, void* dXp, int H, int F, hipStream_t st);
 // dW_gate[e] += Xp_e^T da_e, dW_up[e] += Xp_e^T du_e; with init (bf16 only)
-// the products are stored instead (dW = ..., zeros for experts with no rows)
+// the products are stored instead (dW = ..., zeros for experts with no rows).
+// With rows != nullptr (bf16 only), Xp is X (x_rows rows): row r of the
+// chunk is row rows[r] / k of X (indexed_rows_ok must hold).
 hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, const void* da,
                          const void* du, float* dWg, float* dWu, int E, int H, int F,
-                         hipStream_t st, bool init = false);
+                         hipStream_t st, bool init = false, const int32_t* rows = nullptr,
+                         int k = 1, int64_t x_rows = 0);
 // dW_down[e] += hg_e^T dYp_e (init as gemm_wgrad_gu)
 hipError_t gemm_wgrad_d(int dtype, const int32_t* offsets, const void* hg, const void* dYp,
                         float* dWd, int E, int H, int F, hipStream_t st, bool init = false);

@@ -169,20 +169,23 @@ def test_bf16_forward_reads_permuted_inputs_in_place():
     """The bf16 forward's gate/up GEMM reads each permuted input row straight
     from X: its workspace holds one H-wide per-chunk buffer (the expert
     outputs) and the debug GATHER stage reports that no gather kernel exists,
-    before any launch."""
+    before any launch.  The bf16 backward reads them from X as well (the
+    recompute and the gate/up weight gradient): one H-wide buffer (dY rows,
+    then dXp) besides its three F-wide ones."""
     L = B.lib()
     N, H, F, E, k, c, K_max = 4096, 2048, 1408, 64, 8, 1024, 8
     p = B.moe_plan_chunks(N, H, F, E, k, c, K_max, B.MOE_BF16)
     rows = k * p.c_eff
     hbuf, fbuf = rows * H * 2, rows * F * 2
     assert hbuf + fbuf <= p.fwd_workspace_bytes < 2 * hbuf + fbuf
-    assert p.bwd_workspace_bytes >= 2 * hbuf  # the backward keeps both H-wide buffers
+    assert hbuf + 3 * fbuf <= p.bwd_workspace_bytes < 2 * hbuf + 3 * fbuf
     fake = ctypes.c_void_p(0x100000)  # never dereferenced
     assert L.moe_debug_stage(ctypes.byref(p), 3, 0, *([fake] * 9), fake, p.fwd_workspace_bytes,
                              None) == B.MOE_EUNSUPPORTED
     # fp32 keeps the explicit gather and both buffers
     q = B.moe_plan_chunks(256, 64, 128, 8, 2, 64, 8, B.MOE_F32)
     assert q.fwd_workspace_bytes >= 2 * 2 * q.c_eff * 64 * 4
+    assert q.bwd_workspace_bytes >= 2 * 2 * q.c_eff * 64 * 4
 
 
 def test_status_strings():
