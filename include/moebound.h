@@ -98,8 +98,8 @@ typedef struct moe_stats {
     int64_t max_pairs_per_chunk; /* largest R_i = k * n_i over the chunks     */
     int64_t dispatch_bytes;      /* H-wide per-chunk dispatch buffers carved:
                                     k*c_eff*H*b each; one in bf16 (expert
-                                    outputs, or dY rows then dXp; inputs read
-                                    from X in place), two otherwise           */
+                                    outputs, or dXp; the permuted rows of X
+                                    and dY read in place), two otherwise      */
     int64_t dispatch_bound_bytes;/* 2 * k * c_eff * H * b                     */
     int64_t intermediate_bytes;  /* F-wide per-chunk intermediates            */
     int64_t workspace_bytes;     /* workspace bytes the call used             */

@@ -326,16 +326,20 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
       MOE_CHECK(launch_gather(P.dtype, X, xp, topk_idx, pb.pos, P.E, P.K, i, g.n, P.k, P.H, st));
       MOE_CHECK(gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, a, u, P.H, P.F, st));
     }
-    // backward through the chunk
-    MOE_CHECK(launch_gather(P.dtype, dY, o, topk_idx, pb.pos, P.E, P.K, i, g.n, P.k, P.H, st));
+    // backward through the chunk (bf16 reads the dY rows through perm; the
+    // gathered copy's buffer then only receives dXp)
+    if (!fused)
+      MOE_CHECK(launch_gather(P.dtype, dY, o, topk_idx, pb.pos, P.E, P.K, i, g.n, P.k, P.H, st));
     if (fused_swiglu) {
-      MOE_CHECK(gemm_dh_swiglu(rg, o, W_down, a, u, h, perm_i, gates, dgp, (int64_t)P.k * P.c_eff,
-                               P.N * P.k, P.H, P.F, st));
+      MOE_CHECK(gemm_dh_swiglu(rg, fused ? dY : o, W_down, a, u, h, perm_i, gates, dgp,
+                               (int64_t)P.k * P.c_eff, P.N * P.k, P.H, P.F, st, P.k,
+                               fused ? P.N : 0));
     } else {
       MOE_CHECK(gemm_dh(P.dtype, rg, o, W_down, dh, P.H, P.F, st));
       MOE_CHECK(launch_swiglu_bwd(P.dtype, dh, a, u, h, perm_i, gates, dg, R, P.F, P.N * P.k, st));
     }
-    MOE_CHECK(gemm_wgrad_d(P.dtype, rg.offsets, h, o, dW_down, P.E, P.H, P.F, st, wg_init && i == 0));
+    MOE_CHECK(gemm_wgrad_d(P.dtype, rg.offsets, h, fused ? dY : o, dW_down, P.E, P.H, P.F, st,
+                           wg_init && i == 0, fused ? perm_i : nullptr, P.k, P.N));
     MOE_CHECK(gemm_wgrad_gu(P.dtype, rg.offsets, fused ? X : xp, a, u, dW_gate, dW_up, P.E, P.H,
                             P.F, st, wg_init && i == 0, fused ? perm_i : nullptr, P.k, P.N));
     MOE_CHECK(gemm_dx(P.dtype, rg, a, u, W_gate, W_up, o, P.H, P.F, st));

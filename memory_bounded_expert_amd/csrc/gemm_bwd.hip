@@ -51,11 +51,21 @@ hipError_t wgu_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
   return launch_lds<MODE, Shape<BM, 64, 2, 4, 64, 1>, true, false, false, false, Epi::AccF32>(p, grid, st);
 }
 
-template <int BM>
+template <int BM, Mode MODE>
 hipError_t wd_bf16(const Params& p, dim3 grid, int bn, hipStream_t st) {
-  if (bn == 256) return launch_lds<Mode::Expert, Shape<BM, 256, 2, 2, 32, 2>, false, false, false, false, Epi::AccF32>(p, grid, st);
-  if (bn == 128) return launch_lds<Mode::Expert, Shape<BM, 128, 2, 4, 64, 1>, false, false, false, false, Epi::AccF32>(p, grid, st);
-  return launch_lds<Mode::Expert, Shape<BM, 64, 2, 4, 64, 1>, false, false, false, false, Epi::AccF32>(p, grid, st);
+  if (bn == 256) return launch_lds<MODE, Shape<BM, 256, 2, 2, 32, 2>, false, false, false, false, Epi::AccF32>(p, grid, st);
+  if (bn == 128) return launch_lds<MODE, Shape<BM, 128, 2, 4, 64, 1>, false, false, false, false, Epi::AccF32>(p, grid, st);
+  return launch_lds<MODE, Shape<BM, 64, 2, 4, 64, 1>, false, false, false, false, Epi::AccF32>(p, grid, st);
+}
+
+// K-rows read through rows[r] / k of a x_rows-row source: the division as
+// a multiply-shift, exact while every rows[r] * k < 2^32 (rows[r] < x_rows k)
+bool set_k_rows(Params& p, const int32_t* rows, int k, int64_t x_rows) {
+  if (k < 1 || x_rows < 1 || !indexed_rows_ok(x_rows, k)) return false;
+  p.k_rows = rows;
+  p.k_row_mul = k == 1 ? 0u : (uint32_t)(((1ull << 32) + (uint64_t)k - 1) / (uint64_t)k);
+  p.k_src_rows = x_rows;
+  return true;
 }
 
 template <typename T>
@@ -107,10 +117,15 @@ int dh_ntiles(const RowsGeom& g, int F) {
 
 hipError_t gemm_dh_swiglu(const RowsGeom& g, const void* dYp, const void* Wd, void* a_da,
                           void* u_du, void* h_hg, const int32_t* perm, const float* gates,
-                          float* dgp, int64_t rows, int64_t Nk, int H, int F, hipStream_t st) {
+                          float* dgp, int64_t rows, int64_t Nk, int H, int F, hipStream_t st,
+                          int k, int64_t x_rows) {
   if (g.grid_m == 0) return hipSuccess;
   Params p{};
   p.A = dYp; p.lda = H;
+  if (x_rows > 0) {  // row r of the chunk is row perm[r] / k of dY
+    if (k < 1) return hipErrorInvalidValue;
+    p.a_rows = perm; p.a_row_div = k; p.a_src_rows = x_rows;
+  }
   p.B = Wd; p.ldb = H; p.b_estride = (int64_t)F * H;  // row f of W_down[e] holds K = H
   p.C = h_hg; p.C2 = a_da; p.C3 = u_du; p.ldc = F;
   p.N = F; p.K = H;
@@ -144,15 +159,7 @@ hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, cons
   Params p{};
   p.acc_init = init ? 1 : 0;
   p.A = Xp; p.lda = H;
-  if (rows) {
-    // K-row r is row rows[r] / k of X: the division as a multiply-shift,
-    // exact while every rows[r] * k < 2^32 (rows[r] < x_rows * k)
-    if (dtype != MOE_BF16 || k < 1 || x_rows < 1 || !indexed_rows_ok(x_rows, k))
-      return hipErrorInvalidValue;
-    p.k_rows = rows;
-    p.k_row_mul = ((1ull << 32) + (uint64_t)k - 1) / (uint64_t)k;
-    p.k_src_rows = x_rows;
-  }
+  if (rows && (dtype != MOE_BF16 || !set_k_rows(p, rows, k, x_rows))) return hipErrorInvalidValue;
   p.B = da; p.B2 = du; p.ldb = F;
   p.C = dWg; p.C2 = dWu; p.ldc = F; p.c_estride = (int64_t)H * F;
   p.M = H; p.N = F;
@@ -170,9 +177,11 @@ hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, cons
 }
 
 hipError_t gemm_wgrad_d(int dtype, const int32_t* offsets, const void* hg, const void* dYp,
-                        float* dWd, int E, int H, int F, hipStream_t st, bool init) {
+                        float* dWd, int E, int H, int F, hipStream_t st, bool init,
+                        const int32_t* rows, int k, int64_t x_rows) {
   if (init && dtype != MOE_BF16) return hipErrorInvalidValue;
   Params p{};
+  if (rows && (dtype != MOE_BF16 || !set_k_rows(p, rows, k, x_rows))) return hipErrorInvalidValue;
   p.acc_init = init ? 1 : 0;
   p.A = hg; p.lda = F;
   p.B = dYp; p.ldb = H;
@@ -183,7 +192,10 @@ hipError_t gemm_wgrad_d(int dtype, const int32_t* offsets, const void* hg, const
   const int bn = pick_bn(H, true);
   const dim3 grid((unsigned)(F / bm), (unsigned)(H / bn), (unsigned)E);
   if (dtype == MOE_BF16)
-    return bm == 128 ? wd_bf16<128>(p, grid, bn, st) : wd_bf16<64>(p, grid, bn, st);
+    return rows ? (bm == 128 ? wd_bf16<128, Mode::ExpertIdxB>(p, grid, bn, st)
+                             : wd_bf16<64, Mode::ExpertIdxB>(p, grid, bn, st))
+                : (bm == 128 ? wd_bf16<128, Mode::Expert>(p, grid, bn, st)
+                             : wd_bf16<64, Mode::Expert>(p, grid, bn, st));
   return bm == 128 ? wd_t<float, 128>(p, grid, bn, st) : wd_t<float, 64>(p, grid, bn, st);
 }
 

@@ -43,9 +43,10 @@
 namespace moe {
 namespace gemm {
 
-// ExpertIdx: Expert with the M-contiguous A operand's K-rows read through a
-// row index (Params::k_rows; LDS pipeline only).
-enum class Mode { Rows, Dense, Expert, ExpertIdx };
+// ExpertIdx / ExpertIdxB: Expert with the K-rows of the M-contiguous A, or
+// of the N-contiguous B, read through a row index (Params::k_rows; LDS
+// pipeline only).
+enum class Mode { Rows, Dense, Expert, ExpertIdx, ExpertIdxB };
 // CEStats and CEGrad are the vocabulary-strip cross-entropy epilogues (LDS
 // pipeline, Dense mode only).
 // SwiGLUBwd is the SwiGLU backward fused into dY W_down^T (LDS pipeline,
@@ -102,13 +103,14 @@ struct Params {
   float* sw_dgp;
   int64_t sw_rows;
   int64_t sw_nk;
-  // Mode::ExpertIdx: K-row r of expert e's segment (row offsets[e] + r of
-  // the chunk) is row floor(k_rows[offsets[e] + r] / d) of the k_src_rows-row
-  // matrix at A (instead of row offsets[e] + r of A).  k_row_mul =
-  // ceil(2^32 / d), so that floor(n / d) = (n * k_row_mul) >> 32, exact for
-  // n * d < 2^32.
+  // Mode::ExpertIdx (ExpertIdxB): K-row r of expert e's segment (row
+  // offsets[e] + r of the chunk) is row floor(k_rows[offsets[e] + r] / d) of
+  // the k_src_rows-row matrix at A (B), instead of row offsets[e] + r.
+  // k_row_mul = ceil(2^32 / d) for d >= 2 (0 for d = 1), so that
+  // floor(n / d) = mulhi(n, k_row_mul), exact for n * d < 2^32; the source's
+  // bytes must stay below 2^31.
   const int32_t* k_rows;
-  uint64_t k_row_mul;
+  uint32_t k_row_mul;
   int64_t k_src_rows;
   // Epi::Store in Mode::Rows: row r (of the chunk) is multiplied by
   // row_scale[r] in fp32 before its one rounding (nullptr: unscaled).  The

@@ -200,10 +200,12 @@ __device__ __forceinline__ int kswz(int r) {
   else return (r >> 2) & 3;
 }
 
-// Row-indexed K (Mode::ExpertIdx): K-rows per wave per K-tile (a wave's A
-// loads of an M-contiguous tile cover BK / WAVES consecutive rows), and the
+// Row-indexed K (Mode::ExpertIdx, ExpertIdxB): K-rows per wave per K-tile (a
+// wave's loads of an M-contiguous A or one N-contiguous B tile cover BK /
+// WAVES consecutive rows), and the
 // slots' place and size in LDS (past the stages; per wave, one 256-byte slot
 // per stage, since a dword load into LDS writes all 64 lanes).
+constexpr bool mode_kidx(Mode m) { return m == Mode::ExpertIdx || m == Mode::ExpertIdxB; }
 template <int BK, int WAVES>
 constexpr int kidx_rows() {
   static_assert(BK % WAVES == 0 && BK / WAVES <= 64, "index rows per wave");
@@ -213,8 +215,8 @@ template <class C>
 constexpr int kidx_offset() { return C::NS * C::STAGE; }
 template <Mode MODE, class S, bool DUAL>
 constexpr int lds_bytes() {
-  using C = LdsCfg<S, DUAL, MODE == Mode::ExpertIdx>;
-  constexpr int b = C::NS * C::STAGE + (MODE == Mode::ExpertIdx ? C::WAVES * C::NS * 256 : 0);
+  using C = LdsCfg<S, DUAL, mode_kidx(MODE)>;
+  constexpr int b = C::NS * C::STAGE + (mode_kidx(MODE) ? C::WAVES * C::NS * 256 : 0);
   static_assert(b <= kLdsBytes / S::WG_PER_CU, "LDS over the work-group's share");
   return b;
 }
@@ -224,7 +226,7 @@ constexpr int lds_bytes() {
 // read blockIdx themselves.
 template <Mode MODE, class S, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
 __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
-  using C = LdsCfg<S, DUAL, MODE == Mode::ExpertIdx>;
+  using C = LdsCfg<S, DUAL, mode_kidx(MODE)>;
   using T = bf16_t;
   constexpr int BM = S::BM, BN = S::BN, BK = S::BK, NB = C::NB, NS = C::NS, CK = C::CK;
   constexpr int WM = BM / S::WGM, WN = BN / S::WGN;
@@ -236,9 +238,11 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   static_assert(!(DUAL && KCAT), "DUAL and KCAT are exclusive");
   static_assert(!(DUAL && B_K), "DUAL needs an N-contiguous B");
   static_assert(A_K || RCA >= 8, "M-contiguous A needs BM >= 64");
-  constexpr bool EXPERT = MODE == Mode::Expert || MODE == Mode::ExpertIdx;
-  constexpr bool KIDX = MODE == Mode::ExpertIdx;
-  static_assert(!KIDX || (!A_K && !KCAT), "row-indexed K needs an M-contiguous A");
+  constexpr bool KIDX_A = MODE == Mode::ExpertIdx, KIDX_B = MODE == Mode::ExpertIdxB;
+  constexpr bool KIDX = KIDX_A || KIDX_B;
+  constexpr bool EXPERT = MODE == Mode::Expert || KIDX;
+  static_assert(!KIDX_A || (!A_K && !KCAT), "row-indexed K needs an M-contiguous A");
+  static_assert(!KIDX_B || (!B_K && !DUAL && !KCAT), "row-indexed K needs one N-contiguous B");
   // loads per thread per K-tile (an indexed product adds its index block)
   constexpr int PT = C::PER_TILE + (KIDX ? 1 : 0);
   static_assert(B_K || RCB >= 8, "N-contiguous B needs BN >= 64");
@@ -326,7 +330,7 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
       }
     }
     rA2 = KCAT ? make_srd(A2p + (int64_t)m0 * p.lda, rows * p.lda * TS) : rA;
-  } else if constexpr (KIDX) {
+  } else if constexpr (KIDX_A) {
     // the whole source matrix from column m0: row offsets come per K-row
     rA = make_srd(Ap + m0, (p.k_src_rows * p.lda - m0) * TS);
     rA2 = rA;
@@ -342,15 +346,20 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   } else {
     const int64_t rows = EXPERT ? (int64_t)k_len : (int64_t)p.K;
     const int64_t kb = EXPERT ? k_begin : 0;
-    rB = make_srd(Bp + kb * p.ldb + n0, (MODE == Mode::Dense ? (int64_t)k_len : rows) * p.ldb * TS);
+    if constexpr (KIDX_B) {
+      // the whole source matrix from column n0: row offsets come per K-row
+      rB = make_srd(Bp + n0, (p.k_src_rows * p.ldb - n0) * TS);
+    } else {
+      rB = make_srd(Bp + kb * p.ldb + n0, (MODE == Mode::Dense ? (int64_t)k_len : rows) * p.ldb * TS);
+    }
     rB2 = DUAL ? make_srd(B2p + kb * p.ldb + n0, rows * p.ldb * TS) : rB;
   }
 
   auto stage_a = [&](int s) -> unsigned char* { return smem + s * C::STAGE; };
   auto stage_b = [&](int s) -> unsigned char* { return smem + s * C::STAGE + C::A_BYTES; };
 
-  // ---- row-indexed K (Mode::ExpertIdx).  A wave's A loads of a K-tile cover
-  // KW consecutive K-rows.  Each wave keeps the k_rows entries of
+  // ---- row-indexed K (Mode::ExpertIdx: A; ExpertIdxB: B).  A wave's loads
+  // of that operand's K-tile cover KW consecutive K-rows.  Each wave keeps the k_rows entries of
   // its own rows in private LDS slots past the stages, one 256-byte slot per
   // stage: the slot of stage s holds the entries of the tile that stage s
   // receives next.  issue() reads its rows' entries from the slot, then
@@ -360,10 +369,18 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   constexpr int KW = kidx_rows<BK, C::WAVES>();
   i32x4_t rI{};
   uint32_t ibase = 0;  // this lane's first entry in slot 0 (LDS address)
+  // entry n -> byte offset of its source row (kOob past the source), in
+  // 32-bit arithmetic: the source's bytes stay below 2^31
+  const uint32_t krow_bytes = (uint32_t)((KIDX_A ? p.lda : p.ldb) * TS);
+  const uint32_t ksrc_rows = (uint32_t)p.k_src_rows;
+  auto src_offset = [&](uint32_t n) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t src = p.k_row_mul ? __umulhi(n, p.k_row_mul) : n;
+    return src < ksrc_rows ? src * krow_bytes : kOob;
+  };
   if constexpr (KIDX) {
     rI = make_srd(p.k_rows + k_begin, (int64_t)k_len * 4);
     ibase = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_p)smem) + kidx_offset<C>() +
-            (uint32_t)(wave * NS * 256 + (lane / RCA) * 4);
+            (uint32_t)(wave * NS * 256 + (lane / (KIDX_A ? RCA : RCB)) * 4);
   }
   auto load_idx = [&](int kt, int s) __attribute__((always_inline)) {
     const int r = kt * BK + wave * KW + lane;
@@ -397,14 +414,12 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
         const int c = (lane % RCA) ^ trswz<RCA>(k);
         const int kr = k0 + k;
         uint32_t off;
-        if constexpr (KIDX) {
+        if constexpr (KIDX_A) {
           // row k of the tile is entry u * RPI + lane / RCA of this wave's slot
-          const int32_t n = *reinterpret_cast<const __attribute__((address_space(3))) int32_t*>(
+          const uint32_t n = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
               (uintptr_t)(ibase + (uint32_t)(s * 256 + u * RPI * 4)));
-          const uint64_t src = ((uint64_t)(uint32_t)n * p.k_row_mul) >> 32;
-          off = (kr < k_len && src < (uint64_t)p.k_src_rows)
-                    ? (uint32_t)(((int64_t)src * p.lda + c * 8) * TS)
-                    : kOob;
+          const uint32_t ro = src_offset(n);
+          off = (kr < k_len && ro != kOob) ? ro + (uint32_t)(c * 8 * TS) : kOob;
         } else {
           off = kr < k_len ? (uint32_t)((kr * p.lda + c * 8) * TS) : kOob;
         }
@@ -432,7 +447,17 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
         bool ok = true;
         if constexpr (EXPERT) ok = kr < k_len;
         if constexpr (MODE == Mode::Dense) ok = n0 + c * 8 < p.N;
-        const uint32_t off = ok ? (uint32_t)((kr * p.ldb + c * 8) * TS) : kOob;
+        uint32_t off;
+        if constexpr (KIDX_B) {
+          // row k of the tile is entry u * RPI + lane / RCB of this wave's
+          // slot (one group: ins = wave * B_PW + u)
+          const uint32_t n = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
+              (uintptr_t)(ibase + (uint32_t)(s * 256 + u * RPI * 4)));
+          const uint32_t ro = src_offset(n);
+          off = (ok && ro != kOob) ? ro + (uint32_t)(c * 8 * TS) : kOob;
+        } else {
+          off = ok ? (uint32_t)((kr * p.ldb + c * 8) * TS) : kOob;
+        }
         lds_load16((DUAL && g) ? rB2 : rB, dst, off);
       }
     }
@@ -1012,7 +1037,7 @@ hipError_t set_lds_attr(KERN kern, int lds, bool& done) {
 
 template <Mode MODE, class S, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
 hipError_t launch_lds(const Params& p, dim3 grid, hipStream_t st) {
-  using C = LdsCfg<S, DUAL, MODE == Mode::ExpertIdx>;
+  using C = LdsCfg<S, DUAL, mode_kidx(MODE)>;
   auto kern = gemm_lds_kernel<MODE, S, DUAL, A_K, B_K, KCAT, EPI>;
   constexpr int lds = lds_bytes<MODE, S, DUAL>();
   static bool attr_set = false;

@@ -67,7 +67,9 @@ inline bool indexed_rows_ok(int64_t x_rows, int k) {
 }
 
 // The bf16 backward also reads the permuted inputs from X (the recompute's
-// gate/up GEMM and the gate/up weight gradient), so it keeps no Xp either.
+// gate/up GEMM and the gate/up weight gradient), so it keeps no Xp either,
+// and the permuted output gradients from dY (the dh GEMM and the down weight
+// gradient), so no gather runs.
 inline bool fused_gather_bwd(const moe_plan_t& p) {
   return fused_gather(p) && indexed_rows_ok(p.N, p.k);
 }
@@ -219,9 +221,12 @@ hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd
 // launch_swiglu_bwd, dh' never stored): da, du, g h over a, u, h; the per
 // N-tile shares of dgate into dgp [dh_ntiles][rows].
 int dh_ntiles(const RowsGeom& g, int F);
+// With x_rows > 0, dYp is not a buffer: row r of the chunk is row perm[r] / k
+// of the x_rows-row dY, read straight from it.
 hipError_t gemm_dh_swiglu(const RowsGeom& g, const void* dYp, const void* Wd, void* a_da,
                           void* u_du, void* h_hg, const int32_t* perm, const float* gates,
-                          float* dgp, int64_t rows, int64_t Nk, int H, int F, hipStream_t st);
+                          float* dgp, int64_t rows, int64_t Nk, int H, int F, hipStream_t st,
+                          int k = 1, int64_t x_rows = 0);
 // dXp = da W_gate[e]^T + du W_up[e]^T
 hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du, const void* Wg,
                    const void* Wu, void* dXp, int H, int F, hipStream_t st);
@@ -233,9 +238,12 @@ hipError_t gemm_wgrad_gu(int dtype, const int32_t* offsets, const void* Xp, cons
                          const void* du, float* dWg, float* dWu, int E, int H, int F,
                          hipStream_t st, bool init = false, const int32_t* rows = nullptr,
                          int k = 1, int64_t x_rows = 0);
-// dW_down[e] += hg_e^T dYp_e (init as gemm_wgrad_gu)
+// dW_down[e] += hg_e^T dYp_e (init as gemm_wgrad_gu).  With rows != nullptr
+// (bf16 only), dYp is dY (x_rows rows): row r of the chunk is row rows[r] / k
+// of dY (indexed_rows_ok must hold).
 hipError_t gemm_wgrad_d(int dtype, const int32_t* offsets, const void* hg, const void* dYp,
-                        float* dWd, int E, int H, int F, hipStream_t st, bool init = false);
+                        float* dWd, int E, int H, int F, hipStream_t st, bool init = false,
+                        const int32_t* rows = nullptr, int k = 1, int64_t x_rows = 0);
 // logits = X W_r (+ bias), fp32 out.  With S > 1 (bf16 only) the product is
 // split over K: parts[s] = X[:, s H/S : (s+1) H/S] W_r[s H/S : (s+1) H/S, :]
 // for s < S ([S][N][E] fp32, no bias), and launch_topk adds them up.

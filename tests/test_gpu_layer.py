@@ -57,6 +57,9 @@ def _sample_tokens(N, n=40, seed=0):
     return np.unique(np.concatenate([[0, 1, N - 1], rng.choice(N, n, replace=False)]))
 
 
+DW_ROWS_MAX = 70000
+
+
 def run_workload(name, full=True, wl=None, reduced=None):
     require_lib()
     wl = datagen.WORKLOADS[name] if wl is None else wl
@@ -162,7 +165,11 @@ def run_workload(name, full=True, wl=None, reduced=None):
             assert e_ <= tol, key
         gnp = g.cpu().numpy().astype(np.float64)
         counts = np.bincount(idx_np.reshape(-1), minlength=wl.E)
-        for e in sorted({int(np.argmax(counts)), int(np.argmin(counts)), 7 % wl.E}):
+        # the most-routed expert with at most DW_ROWS_MAX rows (the fp64
+        # oracle's weight gradients over them take seconds), the least-routed
+        # one, and one more
+        hot = int(np.argmax(np.where(counts <= DW_ROWS_MAX, counts, -1)))
+        for e in sorted({hot, int(np.argmin(counts)), 7 % wl.E}):
             rt, rs = np.nonzero(idx_np == e)
             _, dWg, dWu, dWd, _ = oracle.expert_grads(inp.to_f64(inp.X[rt]), inp.to_f64(inp.dY[rt]),
                                                       gnp[rt, rs], *inp.expert_f64(e))
@@ -253,13 +260,15 @@ def test_split_tile_lists_bf16():
 
 # X of 2^31 bytes or more does not fit one buffer resource, so the bf16
 # forward gathers the permuted rows into their buffer (two H-wide buffers, the
-# whole bound) instead of reading them from X inside the GEMM.  524,800 tokens
-# of H = 2048 (X = 2.15 GB), 128 experts under Zipf(1.2) routing, top-2, in
-# K = 8 chunks of 65,600 tokens: 256-row tiles with the split lists (the
-# coldest experts keep segments of at most 128 rows).  Forward only: the
-# backward always gathers.
+# whole bound) instead of reading them from X inside the GEMM, and the
+# backward gathers the X and dY rows (the recompute, the dh GEMM and the
+# weight gradients then read the buffers, not X and dY through perm).
+# 524,800 tokens of H = 2048 (X = 2.15 GB), 128 experts under Zipf(1.2)
+# routing, top-2, in K = 8 chunks of 65,600 tokens: 256-row tiles with the
+# split lists (the coldest experts keep segments of at most 128 rows).
 UNFUSED = datagen.WORKLOADS["zipf_bf16"].with_(
-    name="unfused_gather_bf16", N=524800, H=2048, E=128, k=2, F=128, c=65600, K_max=8)
+    name="unfused_gather_bf16", N=524800, H=2048, E=128, k=2, F=128, c=65600, K_max=8,
+    backward=True)
 
 
 def test_unfused_gather_bf16():
