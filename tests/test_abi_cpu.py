@@ -8,6 +8,7 @@ import os
 import subprocess
 import tempfile
 
+import numpy as np
 import pytest
 
 import oracle
@@ -186,6 +187,44 @@ def test_bf16_forward_reads_permuted_inputs_in_place():
     q = B.moe_plan_chunks(256, 64, 128, 8, 2, 64, 8, B.MOE_F32)
     assert q.fwd_workspace_bytes >= 2 * 2 * q.c_eff * 64 * 4
     assert q.bwd_workspace_bytes >= 2 * 2 * q.c_eff * 64 * 4
+
+
+def test_bf16_backward_reads_in_place_within_the_division_guard():
+    """The bf16 backward reads its permuted rows of X and dY through perm and
+    divides each pair index by k with a multiply-shift, exact while N k^2 <
+    2^32.  One token more than that bound and the backward keeps the
+    gathered permuted-input buffer (k c_eff H b bytes more workspace);
+    everything else in the layout changes by a few pair-indexed words."""
+    H, F, E, k, c = 64, 64, 64, 64, 1024
+    n_max = (1 << 32) // (k * k)  # first N with N k^2 >= 2^32
+    K_max = n_max // c
+    a = B.moe_plan_chunks(n_max - 1, H, F, E, k, c, K_max, B.MOE_BF16)
+    b = B.moe_plan_chunks(n_max, H, F, E, k, c, K_max, B.MOE_BF16)
+    assert a.c_eff == b.c_eff == c
+    hbuf = k * c * H * 2
+    assert hbuf <= b.bwd_workspace_bytes - a.bwd_workspace_bytes <= hbuf + 8 * 256
+    # the forward's in-place read has no such guard
+    assert abs(b.fwd_workspace_bytes - a.fwd_workspace_bytes) <= 8 * 256
+
+
+@pytest.mark.parametrize("k", list(range(1, 65)))
+def test_pair_index_division_by_multiply_shift(k):
+    """floor(n / k) = mulhi(n, ceil(2^32 / k)) for every pair index n < x_rows
+    k when x_rows k^2 < 2^32 (k = 1 passes n through): the identity the
+    row-indexed GEMM loads use, checked at the guard's largest x_rows, on
+    both sides of every multiple of k near the top and at random indices."""
+    m = 0 if k == 1 else -(-(1 << 32) // k)
+    x_rows = ((1 << 32) - 1) // (k * k)
+    top = x_rows * k
+    rng = np.random.default_rng(k)
+    ns = set(range(max(0, top - 4 * k - 3), top))
+    ns.update(int(v) for v in rng.integers(0, top, 2000))
+    for q in range(1, 200):
+        for d in (-1, 0, 1):
+            ns.add(min(top - 1, max(0, q * k + d)))
+    for n in ns:
+        got = n if m == 0 else (n * m) >> 32
+        assert got == n // k, (k, n)
 
 
 def test_status_strings():
