@@ -303,15 +303,15 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
   MOE_CHECK(launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st));
   launches += 2;
   void* xp = ws + L.xp;
-  void* o = ws + L.o;  // dY rows, then dXp
+  void* o = ws + L.o;  // dXp (fp32 and the gathering path: the dY rows first)
   void* h = ws + L.h;  // h, then g h
   void* a = ws + L.a;  // a, then da
   void* u = ws + L.u;  // u, then du
   float* dh = (float*)(ws + L.dh);
   float* dgp = (float*)(ws + L.dgp);
   const bool fused_swiglu = P.dtype == MOE_BF16;
-  // bf16: the recompute and the gate/up weight gradient read the chunk's
-  // permuted input rows from X through perm (no gather, no Xp)
+  // bf16: the recompute, the dh GEMM and both weight gradients read the
+  // chunk's permuted rows of X and dY through perm (no gather, no Xp)
   const bool fused = fused_gather_bwd(P);
   for (int i = 0; i < P.K; ++i) {
     const ChunkGeom g = chunk_geom(P.N, P.K, P.k, i);

@@ -115,7 +115,7 @@ struct Layout {
   size_t pos = 0;         // [N*k] i32
   size_t row_gates = 0;   // [N*k] f32 forward: gates in permuted-row order
   size_t xp = 0;          // [k c_eff][H]  permuted inputs (dispatch buffer 1)
-  size_t o = 0;           // [k c_eff][H]  expert outputs / dY rows, then dXp (buffer 2)
+  size_t o = 0;           // [k c_eff][H]  expert outputs / (dY rows, then) dXp (buffer 2)
   size_t h = 0;           // [k c_eff][F]  h (forward); h, then g*h (backward)
   size_t a = 0;           // [k c_eff][F]  backward: a, then da
   size_t u = 0;           // [k c_eff][F]  backward: u, then du
