@@ -359,13 +359,14 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   auto stage_b = [&](int s) -> unsigned char* { return smem + s * C::STAGE + C::A_BYTES; };
 
   // ---- row-indexed K (Mode::ExpertIdx: A; ExpertIdxB: B).  A wave's loads
-  // of that operand's K-tile cover KW consecutive K-rows.  Each wave keeps the k_rows entries of
-  // its own rows in private LDS slots past the stages, one 256-byte slot per
-  // stage: the slot of stage s holds the entries of the tile that stage s
-  // receives next.  issue() reads its rows' entries from the slot, then
-  // refills the slot with those of the tile the stage receives NS tiles
-  // later, as one more load of the same K-tile: the pipeline's waits then
-  // also cover the entries (only the wave that loaded a slot reads it).
+  // of that operand's K-tile cover KW consecutive K-rows.  Each wave keeps
+  // the k_rows entries of its own rows in private LDS slots past the stages,
+  // one 256-byte slot per stage: the slot of stage s holds the entries of
+  // the tile that stage s receives next.  issue() reads its rows' entries
+  // from the slot, then refills the slot with those of the tile the stage
+  // receives NS tiles later, as one more load of the same K-tile: the
+  // pipeline's waits then also cover the entries (only the wave that loaded
+  // a slot reads it).
   constexpr int KW = kidx_rows<BK, C::WAVES>();
   i32x4_t rI{};
   uint32_t ibase = 0;  // this lane's first entry in slot 0 (LDS address)
