@@ -5,7 +5,8 @@ through the C ABI, against the full fp64 oracle (forward and backward):
     ragged last chunk;
   * a single token (one chunk of one row per selected expert), fp32;
   * 64 experts with 20 tokens of top-2: most experts have no rows in a chunk;
-  * k = 1 (every gate exactly 1);
+  * k = 1 (every gate exactly 1; the backward's row-indexed loads then take
+    a pair index as its token, with no division);
   * one token per chunk (c = 1, K = N);
   * K_max binding: c = 10 asks for 100 chunks, K_max = 3 gives c_eff = 334;
   * every token routed to the same two experts (a Zipf(12) router bias over
@@ -18,7 +19,9 @@ through the C ABI, against the full fp64 oracle (forward and backward):
     gradients' zero fill.
 
 Each case also checks chunked == unchunked (K_max = 1) bitwise for the
-per-token outputs and run-to-run determinism (run_workload does both)."""
+per-token outputs and run-to-run determinism (run_workload does both).  The
+H = 64 cases run the weight gradients in 64-row tiles, so the row-indexed
+products are exercised in their 64- and 128-row shapes."""
 
 import numpy as np
 import pytest
