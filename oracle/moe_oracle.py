@@ -30,7 +30,7 @@ checked against their own definitions.
 Readings taken where the pages are silent (each is listed with the design
 notes of the repository):
   * top-k order: logit descending, ties to the lower expert index; IEEE
-    comparison, so -0.0 and +0.0 tie;
+    comparison, so -0.0 and +0.0 tie; a NaN logit ranks as -inf;
   * selection is made on the logits, gates are the softmax over all experts
     restricted to the selected ones and renormalised to sum to one;
   * the expert FFN is SwiGLU: (silu(x W_gate) * (x W_up)) W_down, no biases;
@@ -109,8 +109,11 @@ def router_logits(X: np.ndarray, Wr: np.ndarray, bias: Optional[np.ndarray] = No
 
 def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
     """The k experts with the largest logits, slot s = rank s in the order
-    (logit descending, expert index ascending).  Returns int64 [N, k]."""
+    (logit descending, expert index ascending).  A NaN logit is read as -inf
+    (so it ties with -inf and the index decides), which keeps the order total
+    on any input.  Returns int64 [N, k]."""
     l = np.asarray(logits)
+    l = np.where(np.isnan(l), -np.inf, l)
     N, E = l.shape
     if not 1 <= k <= E:
         raise ValueError("need 1 <= k <= E")
@@ -344,6 +347,10 @@ def backward_tokens(x_rows, dy_rows, idx_rows, gate_rows, experts: Callable[[int
 # Rounding bound used to judge routing flips between fp32 and fp64 logits
 # ----------------------------------------------------------------------------
 
+# unit roundoff of binary32 (24-bit significand, round to nearest): 2^-24
+FP32_UNIT_ROUNDOFF = 2.0 ** -24
+
+
 def logit_error_bound(X, Wr, bias=None) -> np.ndarray:
     """Per-token bound tau_t = 2 gamma_H max_e sum_h |x_th w_he| (+ one rounding
     of the bias add), gamma_H = H u / (1 - H u), u = 2^-24: the classical bound
@@ -354,7 +361,7 @@ def logit_error_bound(X, Wr, bias=None) -> np.ndarray:
     X = np.asarray(X, f64)
     Wr = np.asarray(Wr, f64)
     H = X.shape[1]
-    u = 2.0 ** -24
+    u = FP32_UNIT_ROUNDOFF
     gam = H * u / (1 - H * u)
     mag = np.abs(X) @ np.abs(Wr)
     l = X @ Wr

@@ -22,6 +22,24 @@ def test_topk_brute_force_with_ties():
             assert list(idx[t]) == brute_topk_row(l[t], k)
 
 
+def test_topk_nan_reads_as_minus_inf():
+    """NaN logits: brute force over a pure-Python order in which NaN is the
+    same key as -inf (ties broken by index); every row gets k distinct
+    experts."""
+    rng = np.random.default_rng(15)
+    key = lambda v: float("-inf") if v != v else float(v)
+    for _ in range(200):
+        N, E = rng.integers(1, 6), rng.integers(1, 12)
+        k = int(rng.integers(1, E + 1))
+        l = rng.integers(-2, 2, size=(N, E)).astype(np.float64)
+        l[rng.random((N, E)) < 0.3] = np.nan
+        l[rng.random((N, E)) < 0.1] = -np.inf
+        idx = oracle.topk_select(l, k)
+        for t in range(N):
+            assert list(idx[t]) == sorted(range(E), key=lambda e: (-key(l[t, e]), e))[:k]
+            assert len(set(idx[t].tolist())) == k
+
+
 def test_topk_defining_property():
     rng = np.random.default_rng(6)
     l = rng.standard_normal((50, 17))
@@ -111,3 +129,54 @@ def test_logit_error_bound_covers_fp32_sums():
         acc = (acc + np.float32(1) * (X[:, h:h + 1] * Wr[h:h + 1, :]).astype(np.float32)).astype(np.float32)
     tau = oracle.logit_error_bound(X, Wr)
     assert np.all(np.abs(acc - l64).max(1) <= tau / 2)
+
+
+def _tight_case():
+    """Two exact products whose fp32 sum rounds by exactly one unit roundoff:
+    1 + 2^-24 is the midpoint between 1 and the next binary32 number, and
+    round-to-nearest-even returns 1.  Returns (X, Wr, fp32 error)."""
+    X = np.array([[1.0, 2.0 ** -24]], np.float32)
+    Wr = np.array([[1.0], [1.0]], np.float32)
+    s32 = np.float32(X[0, 0] * Wr[0, 0]) + np.float32(X[0, 1] * Wr[1, 0])
+    err = abs(float(s32) - (1.0 + 2.0 ** -24))
+    return X, Wr, err
+
+
+def test_logit_error_bound_closed_form():
+    """Pinned from above by the classical bound's value on a 2-term sum.
+    With X = [[1, 1]] and W_r = [[1], [1]]: sum |x w| = 2, l = 2, so
+    tau = 2 (gamma_2 * 2 + u * 2), gamma_n = n u / (1 - n u), where u is the
+    binary32 unit roundoff, taken here from numpy's float32 epsilon (eps / 2)
+    rather than from the oracle."""
+    u = float(np.finfo(np.float32).eps) / 2
+    g2 = 2 * u / (1 - 2 * u)
+    tau = oracle.logit_error_bound(np.array([[1.0, 1.0]]), np.array([[1.0], [1.0]]))
+    assert tau.shape == (1,)
+    assert tau[0] == 2 * (g2 * 2 + u * 2)
+    # with a bias of 0.5: sum |x w| + |b| = 2.5, l = 2.5
+    tb = oracle.logit_error_bound(np.array([[1.0, 1.0]]), np.array([[1.0], [1.0]]),
+                                  np.array([0.5]))
+    np.testing.assert_allclose(tb[0], 2 * (g2 * 2.5 + u * 2.5), rtol=1e-15, atol=0)
+
+
+def test_logit_error_bound_is_nearly_attained():
+    """Pinned from above by a real rounding error: a 2-term fp32 sum whose
+    error is exactly u (a round-half-to-even tie) reaches a third of tau/2
+    (gamma_2 (1 + u) + u (1 + u) ~ 3u).  A bound built on u = 2^-23, or
+    doubled, would sit at a sixth of it and fail."""
+    X, Wr, err = _tight_case()
+    assert err == 2.0 ** -24
+    half = oracle.logit_error_bound(X, Wr)[0] / 2
+    assert err <= half
+    assert err / half >= 0.3333
+
+
+def test_logit_error_bound_planted_wrong_roundoff_is_caught(monkeypatch):
+    """A planted mistake in the oracle (unit roundoff 2^-23 instead of 2^-24)
+    makes the bound too loose; the near-attainment check above catches it."""
+    from oracle import moe_oracle
+
+    X, Wr, err = _tight_case()
+    monkeypatch.setattr(moe_oracle, "FP32_UNIT_ROUNDOFF", 2.0 ** -23)
+    half = moe_oracle.logit_error_bound(X, Wr)[0] / 2
+    assert err / half < 0.3333
