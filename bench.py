@@ -1,19 +1,26 @@
 #!/usr/bin/env python3
-"""Benchmark of the memory-bounded MoE layer forward pass on one MI355X.
+"""Benchmark of the memory-bounded MoE layer on one MI355X.
 
-One step = one full forward pass of the layer (router GEMM, top-k and gates,
-chunk plan, and per chunk: gather (in bf16 folded into the next GEMM's
-operand loads), gate/up grouped GEMM with SwiGLU, down
-grouped GEMM, gate-weighted combine) over one batch of synthetic inputs that
-are resident in HBM before the timed region starts.
+One step = one pass of the layer's whole hot path over one batch of synthetic
+inputs that are resident in HBM before the timed region starts.  For a
+forward+backward workload (the default, `train_bf16`) that is the forward --
+router GEMM, top-k and gates, chunk plan, and per chunk the gate/up grouped
+GEMM with SwiGLU (the permute folded into its operand loads), the down grouped
+GEMM with the gate scaling, the combine -- followed by the backward with
+per-chunk recompute (dX, dW_gate/up/down, dlogits, dgates, dW_r).  Forward-only
+workloads time the forward alone.
 
-Default workload: 4096 tokens, H=2048, 64 experts, top-8, F=1408 SwiGLU,
-c=1024, K_max=8 (K = 4 chunks), bf16 with fp32 accumulation, balanced routing.
-Prints one JSON line on stdout (everything else goes to stderr):
+Default workload: 65,536 tokens, H=2048, 64 experts, top-8, F=1024 SwiGLU,
+c=4096, K_max=16 (K = 16 chunks), bf16 with fp32 accumulation, upstream
+gradient dY ~ N(0, 1).  Prints one JSON line on stdout (everything else goes
+to stderr):
   value = routed token-expert pairs per second (N*k / time per step),
-  roofline = the dominant kernel against its roof (HBM or bf16 MFMA), from
+  roofline = the forward gate/up grouped GEMM against its roof (bf16 MFMA
+             when its arithmetic intensity is above the ridge, else HBM), from
              HIP events around re-launches of that kernel on the layer's stream,
-  cpu_baseline = the fp64 oracle on a bounded sample of the same workload.
+  grouped_gemm = MFMA utilisation of the forward grouped GEMMs,
+  cpu_baseline = the fp64 oracle (forward, and backward for a forward+backward
+             workload) on a bounded token sample of the same workload.
 
 --workload vocab_bf16 (or vocab_small_bf16) benchmarks the vocabulary
 projection with cross-entropy over vocabulary strips instead: one step = the
@@ -39,6 +46,18 @@ FP32_PEAK_TFLOPS = 157.3
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # Sources that decide what the forward GEMM kernels do and how they are
@@ -257,7 +276,9 @@ def cce_main(args, datagen, np, torch, B):
         out["cpu_baseline"] = {"value": round(n_s / cpu_s, 2), "unit": "tokens/s",
                                "cores": threads, "kind": "oracle",
                                "sample": f"first {n_s} of {N} tokens over the whole vocabulary: "
-                                         f"loss, dX and dW, {cpu_s:.1f} s"}
+                                         f"loss, dX and dW, {cpu_s:.1f} s",
+                               "host_cpus": len(os.sched_getaffinity(0)),
+                               "cpu_model": cpu_model()}
         log(f"cpu baseline: {cpu_s:.2f} s, {threads} BLAS threads")
     print(json.dumps(out), flush=True)
 
@@ -413,13 +434,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="balanced_bf16")
+    ap.add_argument("--workload", default="train_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
-                    help="tokens of the batch the oracle runs for the CPU baseline")
+                    help="tokens of the batch the oracle runs for the CPU baseline "
+                         "(forward+backward workloads: at most 2048)")
     ap.add_argument("--stage-reps", type=int, default=5)
     ap.add_argument("--backward", action="store_true",
-                    help="also time forward+backward steps (reported under forward_backward)")
+                    help="forward-only workloads: also time forward+backward steps (reported "
+                         "under forward_backward); a forward+backward workload always does")
     ap.add_argument("--blas-yardstick", action="store_true",
                     help="also time the vendor library's batched GEMM (torch.bmm) on one chunk's "
                          "expert products with equal, contiguous row groups (reported under "
@@ -448,8 +471,12 @@ def main():
     wl = datagen.WORKLOADS[args.workload]
     bf = wl.dtype == "bf16"
     b = 2 if bf else 4
+    # a forward+backward workload's step is the whole hot path: forward, then
+    # backward with per-chunk recompute
+    train = wl.backward
+    want_bwd = train or args.backward
     log(f"generating {wl.name} inputs")
-    inp = datagen.Inputs(wl, dy=args.backward)
+    inp = datagen.Inputs(wl, dy=want_bwd)
 
     def up(a):
         if a is None:
@@ -593,7 +620,7 @@ def main():
             if args.blas_yardstick and bf else None)
 
     fb = None
-    if args.backward:
+    if want_bwd:
         # one step = forward (routing saved) + backward with per-chunk recompute:
         # dX, dW_gate/up/down (fp32), dlogits, dgates and dW_r
         dY = up(inp.dY)
@@ -620,11 +647,13 @@ def main():
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
         e0.record(stream)
         for _ in range(args.steps):
             fbstep()
         e1.record(stream)
         torch.cuda.synchronize()
+        wall_fb = time.perf_counter() - w0
         ms_fb = e0.elapsed_time(e1) / args.steps
         e0.record(stream)
         for _ in range(args.steps):
@@ -635,6 +664,7 @@ def main():
         # backward GEMM flops: 12 H F per pair, plus the 4 H F per pair recompute
         bflops = 16.0 * pairs * wl.H * wl.F
         fb = {"ms_per_step": round(ms_fb, 4), "pairs_per_s": round(pairs / (ms_fb / 1e3), 1),
+              "wall_ms_per_step": round(wall_fb / args.steps * 1e3, 4),
               "backward_ms": round(ms_b, 4),
               "backward_gemm_TFLOP_per_s": round(bflops / (ms_b / 1e3) / 1e12, 1),
               "workspace_bytes": plan.bwd_workspace_bytes}
@@ -642,14 +672,16 @@ def main():
             f"backward {ms_b:.3f} ms ({fb['backward_gemm_TFLOP_per_s']} TFLOP/s over its GEMM flops)")
 
     p1 = B.moe_plan_chunks(wl.N, wl.H, wl.F, wl.E, wl.k, wl.c, 1, plan.dtype)
+    step_ms = fb["ms_per_step"] if train else ms
+    step_wall = fb["wall_ms_per_step"] if train else wall / args.steps * 1e3
     out = {
-        "metric": "routed token-expert pairs/s (forward) at bounded dispatch buffer",
-        "value": round(value, 1),
+        "metric": "routed token-expert pairs/s + grouped-GEMM MFMA util at bounded dispatch buffer",
+        "value": round(pairs / (step_ms / 1e3), 1),
         "unit": "pairs/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -657,14 +689,19 @@ def main():
         "data": "synthetic (seeded normals, bf16-rounded; random-init expert weights)",
         "config": {"workload": wl.name, "N": N, "H": wl.H, "E": wl.E, "top_k": k, "F": wl.F,
                    "c": wl.c, "K_max": wl.K_max, "K": K, "c_eff": plan.c_eff,
+                   "step": "forward+backward" if train else "forward",
                    "parallelism": "single GPU"},
+        "forward": {"ms_per_step": round(ms, 4), "pairs_per_s": round(value, 1)},
         "forward_backward": fb,
         "graph_replay": graph,
         "hbm_copy": hbm_copy,
         "blas_yardstick": yard,
         "roofline": roof,
         "grouped_gemm": {"TFLOP_per_s": round(gemm_flops / gemm_us / 1e6, 1),
-                         "mfma_frac": round(gemm_flops / gemm_us / 1e6 / peak_tf, 4)},
+                         "mfma_frac": round(gemm_flops / gemm_us / 1e6 / peak_tf, 4),
+                         "gate_up_mfma_frac": stages["gemm_up"].get("mfma_frac"),
+                         "down_mfma_frac": stages["gemm_down"].get("mfma_frac"),
+                         "target_mfma_frac": 0.6},
         "dispatch": {"buffer_bytes": stats["dispatch_bytes"],
                      "bound_bytes": plan.dispatch_bound_bytes,
                      "unchunked_buffer_bytes": p1.dispatch_bound_bytes,
@@ -672,30 +709,37 @@ def main():
                      "unchunked_workspace_bytes": p1.fwd_workspace_bytes,
                      "peak_alloc_during_steps": int(peak_extra)},
         "stages": stages,
-        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "wall_ms_per_step": round(step_wall, 4),
     }
 
     if not args.no_cpu_baseline:
         import oracle
         from threadpoolctl import threadpool_info
 
-        n_s = min(args.cpu_tokens, N)
-        log(f"cpu baseline: fp64 oracle on the first {n_s} tokens")
+        n_s = min(args.cpu_tokens, 2048 if train else N, N)
+        what = "forward + backward" if train else "forward"
+        log(f"cpu baseline: fp64 oracle {what} on the first {n_s} tokens")
         X64 = inp.to_f64(inp.X[:n_s])
+        dY64 = inp.to_f64(inp.dY[:n_s]) if train else None
         Wr64 = inp.f64("Wr")
         # repeat the whole sample until about 10 s of CPU work (at most 8 times)
         reps, c0 = 0, time.perf_counter()
         while reps < 8 and (reps == 0 or time.perf_counter() - c0 < 10.0):
-            oracle.moe_forward(X64, Wr64, inp.bias, inp.expert_f64, None, None, k)
+            _, idx_s, g_s, _ = oracle.moe_forward(X64, Wr64, inp.bias, inp.expert_f64, None,
+                                                  None, k)
+            if train:
+                oracle.moe_backward(X64, Wr64, inp.expert_f64, None, None, dY64, idx_s, g_s)
             reps += 1
         cpu_s = time.perf_counter() - c0
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-        out["cpu_baseline"] = {"value": round(reps * n_s * k / cpu_s, 1), "unit": "pairs/s",
-                               "cores": threads, "kind": "oracle",
-                               "sample": f"first {n_s} of {N} tokens, full forward incl. routing "
-                                         f"and fp64 upcast of the weights, {reps} runs in "
-                                         f"{cpu_s:.1f} s"}
-        log(f"cpu baseline: {reps} runs, {cpu_s:.2f} s, {threads} BLAS threads")
+        out["cpu_baseline"] = {
+            "value": round(reps * n_s * k / cpu_s, 1), "unit": "pairs/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"first {n_s} of {N} tokens, full {what} incl. routing and fp64 upcast "
+                      f"of the weights, {reps} runs in {cpu_s:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+        log(f"cpu baseline: {reps} runs, {cpu_s:.2f} s, {threads} BLAS threads on "
+            f"{len(os.sched_getaffinity(0))} host CPUs ({cpu_model()})")
     print(json.dumps(out), flush=True)
 
 

@@ -14,8 +14,9 @@
  *              section 2.1 (expand, permute, recombine), section 3.3
  *              (hop-local recomputation).
  *   [TRILLION] "Training Trillion-Parameter MoE Large Language Models:
- *              End-to-End Optimization Practices": section 3.3 (Permute,
- *              Grouped GEMM, Unpermute).
+ *              End-to-End Optimization Practices": section 1 (896 routed
+ *              experts, 16 activated), section 3.3 (Permute, Grouped GEMM,
+ *              Unpermute).
  *
  * The layer, per token t with input row x_t:
  *   l_t   = x_t W_r (+ bias)                         router logits, fp32
@@ -50,7 +51,8 @@
  *   - Every call returns a moe_status.  Argument errors are found on the
  *     host before anything is enqueued; then outputs are untouched.
  *   - Inputs must be finite.  NaN or Inf inputs give unspecified (but
- *     memory-safe) results.
+ *     memory-safe) values; the routing stays a valid selection (a NaN logit
+ *     ranks as -inf, so each token still gets k distinct experts).
  *   - Calls that share a workspace must not overlap in time.
  */
 #ifndef MOEBOUND_H
@@ -125,6 +127,17 @@ int moe_plan_chunks(int64_t N, int32_t H, int32_t F, int32_t E, int32_t k,
 /*
  * moe_bounded_forward -- the layer's forward pass under the chunk schedule.
  *
+ * Computes, for the whole batch, the router logits and each token's top-k
+ * experts and gates ([RELAY] section 2.1: each token selects its top-k
+ * experts; expanded rows are permuted, processed and recombined), then runs
+ * the [BSO] eq. (1) chunks i = 0..K-1 ("Strided chunk membership") one after
+ * the other: chunk i's routed pairs are permuted into expert-contiguous rows,
+ * pushed through each expert's SwiGLU FFN as grouped GEMMs and combined back
+ * per token, each expert row scaled by its gate ([TRILLION] section 3.3:
+ * Permute, Grouped GEMM, Unpermute).  Per-chunk buffers are sized by
+ * k*c_eff rows ([BSO] "Memory bound"), so the top-k-expanded buffer of the
+ * whole batch never exists.
+ *
  * Inputs (device): X [N][H]; W_r [H][E]; router_bias [E] fp32 or NULL;
  *   W_gate, W_up [E][H][F]; W_down [E][F][H].
  * Outputs (device, overwritten): Y [N][H]; topk_idx [N][k] int32 (S_t in
@@ -185,8 +198,11 @@ const char* moe_status_string(int status);
 
 /*
  * moe_debug_topk -- the router top-k and gate stage alone, for stage-level
- * checks.  logits [N][E] fp32 in; topk_idx [N][k] int32 and gates [N][k]
- * fp32 out, as the forward call computes them.  Errors: MOE_EINVAL for
+ * checks: each token's top-k experts and renormalised gates ([RELAY]
+ * section 2.1, top-k selection; up to the "896 routed experts, 16 activated"
+ * shape of [TRILLION] section 1 and beyond, E <= 1024, k <= 64).
+ * logits [N][E] fp32 in; topk_idx [N][k] int32 and gates [N][k] fp32 out,
+ * as the forward call computes them.  Errors: MOE_EINVAL for
  * N < 0, k < 1, k > E or a NULL pointer with N > 0; MOE_EUNSUPPORTED for
  * E > 1024 or k > 64.
  */

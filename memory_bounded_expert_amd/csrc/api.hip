@@ -228,8 +228,8 @@ MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const voi
   MOE_CHECK(gemm_router(P.dtype, X, W_r, router_bias, lg, P.N, P.H, P.E, st, rparts, rs));
   MOE_CHECK(launch_topk(lg, P.N, P.E, P.k, topk_idx, gates, st, rparts, rs, router_bias));
   const PlanBuffers pb = plan_buffers(ws, L, nullptr, nullptr, nullptr);
-  MOE_CHECK(launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st, gates));
-  launches += 2;
+  if (launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st, gates, &launches) != hipSuccess)
+    return MOE_EHIP;
   const bool fused = fused_gather(P);
   void* xp = ws + L.xp;
   void* o = ws + L.o;
@@ -300,8 +300,8 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
   void* wrt = ws + L.wrt;
   MOE_CHECK(launch_transpose(P.dtype, W_r, wrt, P.H, P.E, st));
   const PlanBuffers pb = plan_buffers(ws, L, nullptr, nullptr, nullptr);
-  MOE_CHECK(launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st));
-  launches += 2;
+  if (launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st, nullptr, &launches) != hipSuccess)
+    return MOE_EHIP;
   void* xp = ws + L.xp;
   void* o = ws + L.o;  // dXp (fp32 and the gathering path: the dY rows first)
   void* h = ws + L.h;  // h, then g h

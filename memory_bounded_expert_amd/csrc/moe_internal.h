@@ -158,10 +158,11 @@ struct PlanBuffers {
   int32_t* long_count;
 };
 // Plans every chunk at once: counts, scans and scatters the whole batch's
-// routed pairs (O(N k) int32, nothing H-wide).  3 launches.
+// routed pairs (O(N k) int32, nothing H-wide) in 3 launches, added to
+// *launches when it is given.
 // With b.row_gates set, also writes each permuted row's gate (gates [N*k]).
 hipError_t launch_plan(const int32_t* idx, int64_t N, int K, int k, int E, const PlanBuffers& b,
-                       hipStream_t st, const float* gates = nullptr);
+                       hipStream_t st, const float* gates = nullptr, int* launches = nullptr);
 
 // Data movement (dtype-dispatched: 0 f32, 1 bf16).
 // Permute (gather) of chunk i: dst[pos[t, s]] = src[t] for each token t of the

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void plan_scatter_kernel(
 }  // namespace
 
 hipError_t launch_plan(const int32_t* idx, int64_t N, int K, int k, int E, const PlanBuffers& b,
-                       hipStream_t st, const float* gates) {
+                       hipStream_t st, const float* gates, int* launches) {
   if (b.row_gates && !gates) return hipErrorInvalidValue;
   if (N == 0) return hipSuccess;
   plan_count_kernel<<<dim3((unsigned)b.nblk, (unsigned)K), kPlanBlock,
@@ -203,6 +203,7 @@ hipError_t launch_plan(const int32_t* idx, int64_t N, int K, int k, int E, const
   const int64_t pairs = N * k;
   plan_scatter_kernel<<<(unsigned)ceil_div(pairs, kThreads), kThreads, 0, st>>>(
       idx, N, K, k, E, b.nblk, b.blk, b.rank, b.perm, b.pos, gates, b.row_gates);
+  if (launches) *launches += 3;
   return hipGetLastError();
 }
 

@@ -3,11 +3,11 @@
 // Each token selects its top-k experts ("Memory-Efficient Expert Routing for
 // Distributed MoE Training", section 2.1).  Slot s holds the s-th expert in
 // the order (logit descending, expert index ascending); IEEE comparison, so
-// -0.0 and +0.0 tie and the lower index wins.  The gates are the softmax of
-// the logits restricted to the selected experts, which equals the softmax over
-// all E experts restricted and renormalised ("896 routed experts, 16
-// activated": "Training Trillion-Parameter MoE ...", section 1, is the widest
-// shape served).
+// -0.0 and +0.0 tie and the lower index wins; a NaN logit ranks as -inf.  The
+// gates are the softmax of the logits restricted to the selected experts,
+// which equals the softmax over all E experts restricted and renormalised
+// ("896 routed experts, 16 activated": "Training Trillion-Parameter MoE ...",
+// section 1, is the widest shape served).
 #include "device_common.hpp"
 #include "moe_internal.h"
 
@@ -20,6 +20,11 @@ struct Cand {
   float v;
   int i;  // INT_MAX: no candidate
 };
+
+// A NaN logit is read as -inf, so that the comparisons below form one total
+// order (logit descending, index ascending) on any input: every token then
+// gets k distinct experts, each slot written once.
+__device__ __forceinline__ float rank_key(float x) { return __builtin_isnan(x) ? -INFINITY : x; }
 
 // (v, i) beats (w, j) when v > w, or v and w do not compare greater either
 // way (equal, or +0/-0) and i < j.
@@ -60,6 +65,7 @@ __global__ __launch_bounds__(kThreads) void topk_gates_kernel(float* __restrict_
       } else {
         v[j] = row[e];
       }
+      v[j] = rank_key(v[j]);
       avail |= 1u << j;
     }
   }
@@ -133,6 +139,7 @@ __global__ __launch_bounds__(kThreads) void topk_rank_kernel(float* __restrict__
     } else {
       v = row[lane];
     }
+    v = rank_key(v);
   }
   sv[w][lane] = v;
   __builtin_amdgcn_wave_barrier();
@@ -177,9 +184,7 @@ hipError_t launch_topk(const float* logits_in, int64_t N, int E, int k, int32_t*
     topk_rank_kernel<<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates, parts, S, bias);
     return hipGetLastError();
   }
-  if (vpl <= 1)
-    topk_gates_kernel<1><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates, parts, S, bias);
-  else if (vpl <= 2)
+  if (vpl <= 2)
     topk_gates_kernel<2><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates, parts, S, bias);
   else if (vpl <= 4)
     topk_gates_kernel<4><<<grid, kThreads, 0, st>>>(logits, N, E, k, idx, gates, parts, S, bias);

@@ -185,9 +185,29 @@ def run_workload(name, full=True, wl=None, reduced=None):
             if a.dtype == torch.bfloat16:
                 a, b_ = a.view(torch.int16), b_.view(torch.int16)
             assert torch.equal(a, b_), key
+        # weight gradients sum over tokens chunk by chunk: their last bits
+        # depend on K, but every expert's (not only the sampled ones') must
+        # agree with the unchunked run to fp32 rounding
         for key in ("dW_gate", "dW_up", "dW_down", "dW_r"):
-            say(f"[{name}]   {key} chunked vs unchunked "
-                f"{rel_err(dev_to_f64(out[key]), dev_to_f64(out1[key])):.2e}")
+            dk = rel_err(dev_to_f64(out[key]), dev_to_f64(out1[key]))
+            say(f"[{name}]   {key} chunked vs unchunked {dk:.2e}")
+            assert dk <= 1e-5, key
+        del out1
+        # dW_r = X^T dlogits over the whole batch, against fp64 on the GPU's
+        # dlogits (checked above on the sampled tokens): within the oracle
+        # tolerance, and elementwise within the rigorous bound of an fp32
+        # sum of N rounded products, gamma_{N+1} (|X|^T |dlogits|)
+        dl = out["dlogits"].cpu().numpy().astype(np.float64)
+        Xf = inp.f64("X")
+        dwr_ref = Xf.T @ dl
+        mag = np.abs(Xf).T @ np.abs(dl)
+        del Xf
+        e_ = rel_err(dev_to_f64(out["dW_r"]), dwr_ref)
+        say(f"[{name}]   full dW_r rel err vs fp64 X^T dlogits {e_:.3e}")
+        assert e_ <= tol
+        u = 2.0 ** -24
+        gam = (wl.N + 1) * u / (1 - (wl.N + 1) * u)
+        assert np.all(np.abs(dev_to_f64(out["dW_r"]) - dwr_ref) <= gam * mag), "dW_r rounding bound"
 
 
 def test_tiny_f32():

@@ -49,6 +49,28 @@ def test_topk_forced_ties():
     assert np.all(g.cpu().numpy() == 1.0)  # k = 1: the gate is exactly one
 
 
+@pytest.mark.parametrize("E", [40, 64, 896])
+def test_topk_nan_logits(E):
+    """NaN logits rank as -inf (both top-k kernels: E <= 64 and above): the
+    selection is bit-exact against the oracle and every slot holds a distinct
+    expert; rows whose selected logits are finite keep finite gates."""
+    require_lib()
+    rng = np.random.default_rng(E)
+    N = 300
+    lg = rng.standard_normal((N, E)).astype(np.float32)
+    lg[rng.random((N, E)) < 0.2] = np.nan
+    lg[:4] = np.nan                  # rows of NaN only
+    lg[4:8, ::3] = -np.inf           # NaN and -inf together
+    for k in (1, 5, 16):
+        say(f"topk NaN E={E} k={k}")
+        idx, g = B.moe_debug_topk(torch.from_numpy(lg).to(DEV), k)
+        idx, g = idx.cpu().numpy(), g.cpu().numpy()
+        assert np.array_equal(idx, oracle.topk_select(lg.astype(np.float64), k))
+        assert all(len(set(r.tolist())) == k for r in idx)
+        fin = np.all(np.isfinite(np.take_along_axis(lg, idx, 1)), axis=1)
+        assert np.all(np.isfinite(g[fin]))
+
+
 @pytest.mark.parametrize("N,E,k,c,K_max", [
     (256, 8, 2, 64, 8),          # tiny workload's plan (K = 4)
     (4096, 64, 8, 1024, 8),      # balanced shape
