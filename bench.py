@@ -113,6 +113,44 @@ def stage_work(stage, wl, b, n_i, R_i, E_i):
     raise KeyError(stage)
 
 
+def bwd_stage_work(stage, wl, b, n_i, R_i, E_i, first):
+    """Algorithmic (bytes, flops) of one launch of a per-chunk backward stage
+    on a chunk with n_i tokens, R_i routed pairs and E_i non-empty experts
+    (first: chunk 0, whose weight-gradient products store dW instead of
+    reading and writing it)."""
+    H, F, E = wl.H, wl.F, wl.E
+    if stage == "recompute":  # weights, X rows; a, u, h out
+        return 2 * E_i * H * F * b + R_i * H * b + 3 * R_i * F * b, 4.0 * R_i * H * F
+    if stage == "dh":  # W_down, dY rows, a/u/h in, da/du/gh out, gates and dgate shares
+        return (E_i * F * H * b + R_i * H * b + 6 * R_i * F * b + R_i * 8
+                + (F // 256) * R_i * 4), 2.0 * R_i * H * F
+    if stage == "wgrad_down":  # g h, dY rows in; fp32 dW_down read + written (chunk 0: written)
+        dw = E * F * H * 4 if first else 2 * E_i * F * H * 4
+        return R_i * F * b + R_i * H * b + R_i * 4 + dw, 2.0 * R_i * H * F
+    if stage == "wgrad_gate_up":  # X rows, da, du in; fp32 dW_gate, dW_up read + written
+        dw = 2 * E * H * F * 4 if first else 4 * E_i * H * F * 4
+        return R_i * H * b + 2 * R_i * F * b + R_i * 4 + dw, 4.0 * R_i * H * F
+    if stage == "dx":  # da, du, W_gate, W_up in; dXp out
+        return 2 * R_i * F * b + 2 * E_i * H * F * b + R_i * H * b, 4.0 * R_i * H * F
+    if stage == "combine_bwd":  # dXp rows in, dX and dlogits rows out, router path
+        return (R_i + n_i) * H * b + n_i * E * 4 + E * H * b + R_i * 12, 2.0 * n_i * wl.k * H
+    if stage == "dwr":  # X rows and dlogits of the chunk's tokens; dW_r read + written
+        return n_i * H * b + n_i * E * 4 + R_i * 4 + 2 * H * E * 4, 2.0 * R_i * H
+    raise KeyError(stage)
+
+
+def roof_of(byts, flops, us, peak_tf):
+    """The stage's roof (bf16 MFMA when its intensity is above the ridge, else
+    HBM) and its achieved fraction of it."""
+    if flops and flops / byts * 1e-3 * HBM_PEAK_GBS > peak_tf:
+        tf = flops / us / 1e6
+        return {"bound": "mfma", "achieved": round(tf, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(tf / peak_tf, 4)}
+    gbs = byts / us / 1e3
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def cce_stage_work(stage, N, H, w):
     """Algorithmic (bytes, flops) of one launch of a vocabulary-strip
     cross-entropy stage on a strip of w vocabulary entries (bf16 X, W and
@@ -670,6 +708,51 @@ def main():
               "workspace_bytes": plan.bwd_workspace_bytes}
         log(f"forward+backward: {ms_fb:.3f} ms/step, {fb['pairs_per_s']:.4g} pairs/s; "
             f"backward {ms_b:.3f} ms ({fb['backward_gemm_TFLOP_per_s']} TFLOP/s over its GEMM flops)")
+
+        # per-kernel: re-launch each backward stage of each chunk in the
+        # backward call's order, one event pair per launch
+        bnames = ["recompute", "dh", "wgrad_down", "wgrad_gate_up", "dx", "combine_bwd", "dwr"]
+        bstep()
+        torch.cuda.synchronize()
+        bmarks = {n_: [] for n_ in bnames}
+        for _ in range(args.stage_reps):
+            lead(2.0 + 0.3 * K * len(bnames))
+            for s_ in ("zero", "transpose", "plan"):
+                B.moe_debug_stage_bwd(plan, s_, 0, X, Wr, Wg, Wu, Wd, dY, idx, gates, grads, wsb,
+                                      stream=stream)
+            for i in range(K):
+                for n_ in bnames:
+                    e0, e1 = ev(), ev()
+                    e0.record(stream)
+                    B.moe_debug_stage_bwd(plan, n_, i, X, Wr, Wg, Wu, Wd, dY, idx, gates, grads,
+                                          wsb, stream=stream)
+                    e1.record(stream)
+                    bmarks[n_].append((e0, e1))
+        torch.cuda.synchronize()
+        bst = {}
+        peak_b = BF16_PEAK_TFLOPS if bf else FP32_PEAK_TFLOPS
+        for n_ in bnames:
+            us = float(np.mean([a.elapsed_time(b_) for a, b_ in bmarks[n_]])) * 1e3
+            work = [bwd_stage_work(n_, wl, b, *c_, first=(ci == 0)) for ci, c_ in enumerate(chunks)]
+            byts = float(np.mean([w_[0] for w_ in work]))
+            flops = float(np.mean([w_[1] for w_ in work]))
+            rec = {"us_per_launch": round(us, 2), "launches_per_step": K,
+                   "alg_bytes_per_launch": int(byts), "GB_per_s": round(byts / us / 1e3, 1),
+                   "alg_flops_per_launch": int(flops), "TFLOP_per_s": round(flops / us / 1e6, 1),
+                   "roof": roof_of(byts, flops, us, peak_b)}
+            bst[n_] = rec
+            log(f"  {n_:13s} {rec}")
+        fb["stages"] = bst
+        # the re-launches reproduce the backward call's outputs bitwise
+        ref_g = {k_: v_.clone() for k_, v_ in grads.items()}
+        bstep()
+        torch.cuda.synchronize()
+        for k_, v_ in grads.items():
+            same = torch.equal(v_.view(torch.int16) if v_.dtype == torch.bfloat16 else v_,
+                               ref_g[k_].view(torch.int16) if v_.dtype == torch.bfloat16
+                               else ref_g[k_])
+            assert same, f"backward stage re-launches changed {k_}"
+        del ref_g
 
     p1 = B.moe_plan_chunks(wl.N, wl.H, wl.F, wl.E, wl.k, wl.c, 1, plan.dtype)
     step_ms = fb["ms_per_step"] if train else ms

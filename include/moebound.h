@@ -261,6 +261,48 @@ int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk,
                     void* Y, int32_t* topk_idx, float* gates,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * moe_debug_stage_bwd -- re-launch one stage of the backward pass (for one
+ * chunk, for the per-chunk stages), for timing its kernels with events on
+ * `stream`.  The stages are the backward call's steps with per-chunk
+ * recompute ([BSO] "Nested gradient checkpointing"; [RELAY] section 3.3):
+ *   MOE_BSTAGE_ZERO         zero dW_r (and, fp32, the expert dW) -- whole call;
+ *   MOE_BSTAGE_TRANSPOSE    W_r^T for the router path of dX -- whole call;
+ *   MOE_BSTAGE_PLAN         the per-chunk permutations -- whole call;
+ *   MOE_BSTAGE_RECOMPUTE    a = Xp W_gate, u = Xp W_up, h = silu(a) u;
+ *   MOE_BSTAGE_DH           dh' = dYp W_down^T with the SwiGLU backward
+ *                           (da, du, g h and the chunk's dgate shares);
+ *   MOE_BSTAGE_WGRAD_DOWN   dW_down += (g h)^T dYp;
+ *   MOE_BSTAGE_WGRAD_GATE_UP dW_gate += Xp^T da, dW_up += Xp^T du;
+ *   MOE_BSTAGE_DX           dXp = da W_gate^T + du W_up^T;
+ *   MOE_BSTAGE_COMBINE_BWD  dX rows (slot order), dgates, dlogits;
+ *   MOE_BSTAGE_DWR          dW_r += X^T dlogits over the chunk's tokens
+ *                           (nothing when dW_r is NULL).
+ * (fp32 plans, and bf16 plans whose X or dY cannot be read in place, also
+ * run the gather of X rows in RECOMPUTE and of dY rows in DH.)
+ * Precondition: the last call that used `workspace` was moe_bounded_backward
+ * with the same plan and arguments (dgates and dW_r NULL or not as there).
+ * Running ZERO, TRANSPOSE, PLAN and then RECOMPUTE .. DWR for chunks
+ * 0..K-1 reproduces that call's outputs bitwise; a stage run out of that
+ * order computes on whatever the buffers hold.
+ * Errors: MOE_EINVAL for a bad plan, stage, chunk (0 <= chunk < plan->K for
+ *   the per-chunk stages), N = 0 or a NULL required pointer; MOE_EWORKSPACE
+ *   as moe_bounded_backward; MOE_EHIP if an enqueue failed.
+ */
+enum moe_bwd_stage {
+    MOE_BSTAGE_ZERO = 0, MOE_BSTAGE_TRANSPOSE = 1, MOE_BSTAGE_PLAN = 2,
+    MOE_BSTAGE_RECOMPUTE = 3, MOE_BSTAGE_DH = 4, MOE_BSTAGE_WGRAD_DOWN = 5,
+    MOE_BSTAGE_WGRAD_GATE_UP = 6, MOE_BSTAGE_DX = 7, MOE_BSTAGE_COMBINE_BWD = 8,
+    MOE_BSTAGE_DWR = 9
+};
+int moe_debug_stage_bwd(const moe_plan_t* plan, int32_t stage, int32_t chunk,
+                        const void* X, const void* W_r,
+                        const void* W_gate, const void* W_up, const void* W_down,
+                        const void* dY, const int32_t* topk_idx, const float* gates,
+                        void* dX, float* dW_gate, float* dW_up, float* dW_down,
+                        float* dlogits, float* dgates, float* dW_r,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

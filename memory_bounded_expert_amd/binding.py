@@ -25,6 +25,8 @@ HEADERS = (os.path.join(INCLUDE, "moebound.h"), os.path.join(INCLUDE, "cce.h"))
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 STAGES = {"router": 0, "topk": 1, "plan": 2, "gather": 3, "gemm_up": 4, "gemm_down": 5,
           "combine": 6}
+BSTAGES = {"zero": 0, "transpose": 1, "plan": 2, "recompute": 3, "dh": 4, "wgrad_down": 5,
+           "wgrad_gate_up": 6, "dx": 7, "combine_bwd": 8, "dwr": 9}
 MOE_F32, MOE_BF16 = 0, 1
 CCE_STAGES = {"logits": 0, "fold": 1, "grad": 2, "dx": 3, "dw": 4}
 
@@ -99,6 +101,9 @@ def lib() -> ctypes.CDLL:
     L.moe_debug_plan.argtypes = [_c.POINTER(MoePlan), _vp, _vp, _vp, _vp, _vp, _c.c_size_t, _vp]
     L.moe_debug_stage.restype = _c.c_int
     L.moe_debug_stage.argtypes = [_c.POINTER(MoePlan), _c.c_int32, _c.c_int32] + [_vp] * 9 + [
+        _vp, _c.c_size_t, _vp]
+    L.moe_debug_stage_bwd.restype = _c.c_int
+    L.moe_debug_stage_bwd.argtypes = [_c.POINTER(MoePlan), _c.c_int32, _c.c_int32] + [_vp] * 15 + [
         _vp, _c.c_size_t, _vp]
     L.cce_plan.restype = _c.c_int
     L.cce_plan.argtypes = [_c.c_int64, _c.c_int32, _c.c_int64, _c.c_int32, _c.c_int32,
@@ -292,6 +297,19 @@ def moe_debug_stage(plan: MoePlan, stage: str, chunk: int, X, W_r, router_bias, 
                                  _ptr(router_bias), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
                                  _ptr(Y), _ptr(topk_idx), _ptr(gates), _ptr(ws), ws.numel(),
                                  _stream(X.device, stream)), "moe_debug_stage")
+
+
+def moe_debug_stage_bwd(plan: MoePlan, stage: str, chunk: int, X, W_r, W_gate, W_up, W_down, dY,
+                        topk_idx, gates, grads: dict, ws, stream=None):
+    """Re-launch one backward stage (for one chunk) on the state of the last
+    backward call on ``ws``; ``grads`` holds that call's output tensors (the
+    dict moe_bounded_backward returns, or the tensors passed to it)."""
+    _check(lib().moe_debug_stage_bwd(
+        ctypes.byref(plan), BSTAGES[stage], chunk, _ptr(X), _ptr(W_r), _ptr(W_gate), _ptr(W_up),
+        _ptr(W_down), _ptr(dY), _ptr(topk_idx), _ptr(gates), _ptr(grads["dX"]),
+        _ptr(grads["dW_gate"]), _ptr(grads["dW_up"]), _ptr(grads["dW_down"]),
+        _ptr(grads["dlogits"]), _ptr(grads.get("dgates")), _ptr(grads.get("dW_r")), _ptr(ws),
+        ws.numel(), _stream(X.device, stream)), "moe_debug_stage_bwd")
 
 
 # ---- vocabulary projection with cross-entropy over vocabulary strips

@@ -201,23 +201,26 @@ MOE_API int moe_plan_chunks(int64_t N, int32_t H, int32_t F, int32_t E, int32_t 
   return MOE_OK;
 }
 
-MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const void* W_r,
-                                const float* router_bias, const void* W_gate, const void* W_up,
-                                const void* W_down, void* Y, int32_t* topk_idx, float* gates,
-                                float* logits, void* workspace, size_t workspace_bytes,
-                                void* stream, moe_stats_t* stats) {
+namespace moe {
+
+int check_forward_args(const moe_plan_t* plan, const void* X, const void* W_r,
+                       const void* W_gate, const void* W_up, const void* W_down, const void* Y,
+                       const int32_t* topk_idx, const float* gates) {
   if (!plan_ok(plan)) return MOE_EINVAL;
-  const moe_plan_t& P = *plan;
+  if (plan->N == 0) return MOE_OK;
+  if (!X || !W_r || !W_gate || !W_up || !W_down || !Y || !topk_idx || !gates) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int forward_impl(const moe_plan_t& P, const void* X, const void* W_r, const float* router_bias,
+                 const void* W_gate, const void* W_up, const void* W_down, void* Y,
+                 int32_t* topk_idx, float* gates, float* logits, void* workspace,
+                 hipStream_t st, moe_stats_t* stats) {
   if (P.N == 0) {
     fill_stats(stats, P, 0, 0, 0);
     return MOE_OK;
   }
-  if (!X || !W_r || !W_gate || !W_up || !W_down || !Y || !topk_idx || !gates || !workspace)
-    return MOE_EINVAL;
-  if ((uintptr_t)workspace % 256) return MOE_EINVAL;
-  if (workspace_bytes < (size_t)P.fwd_workspace_bytes) return MOE_EWORKSPACE;
   const Layout L = make_layout(P, Pass::Forward, logits == nullptr, false);
-  hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   float* lg = logits ? logits : (float*)(ws + L.logits);
   int launches = 0;
@@ -263,6 +266,169 @@ MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const voi
   return MOE_OK;
 }
 
+}  // namespace moe
+
+MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const void* W_r,
+                                const float* router_bias, const void* W_gate, const void* W_up,
+                                const void* W_down, void* Y, int32_t* topk_idx, float* gates,
+                                float* logits, void* workspace, size_t workspace_bytes,
+                                void* stream, moe_stats_t* stats) {
+  if (int s = check_forward_args(plan, X, W_r, W_gate, W_up, W_down, Y, topk_idx, gates))
+    return s;
+  const moe_plan_t& P = *plan;
+  if (P.N > 0) {
+    if (!workspace) return MOE_EINVAL;
+    if ((uintptr_t)workspace % 256) return MOE_EINVAL;
+    if (workspace_bytes < (size_t)P.fwd_workspace_bytes) return MOE_EWORKSPACE;
+  }
+  return forward_impl(P, X, W_r, router_bias, W_gate, W_up, W_down, Y, topk_idx, gates, logits,
+                      workspace, (hipStream_t)stream, stats);
+}
+
+namespace moe {
+namespace {
+
+// Everything one backward call's kernels read and write, resolved once.
+struct BwdCall {
+  const moe_plan_t* P;
+  Layout L;
+  PlanBuffers pb;
+  hipStream_t st;
+  const void *X, *W_r, *W_gate, *W_up, *W_down, *dY;
+  const int32_t* topk_idx;
+  const float* gates;
+  void* dX;
+  float *dW_gate, *dW_up, *dW_down, *dlogits, *dg, *dW_r;
+  void *wrt, *xp, *o, *h, *a, *u;
+  float *dh, *dgp;
+  bool fused;         // bf16: permuted rows of X and dY read through perm
+  bool fused_swiglu;  // bf16: SwiGLU backward in the dh GEMM's epilogue
+  bool wg_init;       // bf16: chunk 0 stores dW instead of accumulating
+};
+
+BwdCall bwd_call(const moe_plan_t& P, const void* X, const void* W_r, const void* W_gate,
+                 const void* W_up, const void* W_down, const void* dY, const int32_t* topk_idx,
+                 const float* gates, void* dX, float* dW_gate, float* dW_up, float* dW_down,
+                 float* dlogits, float* dgates, float* dW_r, void* workspace, hipStream_t st) {
+  BwdCall c;
+  c.P = &P;
+  c.L = make_layout(P, Pass::Backward, false, dgates == nullptr);
+  char* ws = (char*)workspace;
+  c.pb = plan_buffers(ws, c.L, nullptr, nullptr, nullptr);
+  c.st = st;
+  c.X = X; c.W_r = W_r; c.W_gate = W_gate; c.W_up = W_up; c.W_down = W_down; c.dY = dY;
+  c.topk_idx = topk_idx; c.gates = gates; c.dX = dX;
+  c.dW_gate = dW_gate; c.dW_up = dW_up; c.dW_down = dW_down; c.dlogits = dlogits;
+  c.dg = dgates ? dgates : (float*)(ws + c.L.dgates);
+  c.dW_r = dW_r;
+  c.wrt = ws + c.L.wrt;
+  c.xp = ws + c.L.xp;
+  c.o = ws + c.L.o;  // dXp (fp32 and the gathering path: the dY rows first)
+  c.h = ws + c.L.h;  // h, then g h
+  c.a = ws + c.L.a;  // a, then da
+  c.u = ws + c.L.u;  // u, then du
+  c.dh = (float*)(ws + c.L.dh);
+  c.dgp = (float*)(ws + c.L.dgp);
+  c.fused_swiglu = P.dtype == MOE_BF16;
+  c.fused = fused_gather_bwd(P);
+  c.wg_init = P.dtype == MOE_BF16 && P.N > 0;
+  return c;
+}
+
+// Runs backward stage `stage` (enum moe_bwd_stage); the per-chunk stages act
+// on chunk i.  Adds the kernels it enqueues to *launches.
+hipError_t bwd_stage(const BwdCall& c, int stage, int i, int* launches) {
+  const moe_plan_t& P = *c.P;
+  const hipStream_t st = c.st;
+  hipError_t err = hipSuccess;
+  auto run = [&](hipError_t e) {
+    if (err == hipSuccess) {
+      err = e;
+      if (e == hipSuccess) ++*launches;
+    }
+  };
+  if (stage == MOE_BSTAGE_ZERO) {
+    // bf16: chunk 0's weight-gradient products store dW (zeros for experts
+    // without rows) and later chunks accumulate; fp32 accumulates from zero
+    const size_t wbytes = (size_t)P.E * P.H * P.F * sizeof(float);
+    if (!c.wg_init) {
+      run(launch_fill_zero(c.dW_gate, wbytes, st));
+      run(launch_fill_zero(c.dW_up, wbytes, st));
+      run(launch_fill_zero(c.dW_down, wbytes, st));
+    }
+    if (c.dW_r) run(launch_fill_zero(c.dW_r, (size_t)P.H * P.E * sizeof(float), st));
+    return err;
+  }
+  if (stage == MOE_BSTAGE_TRANSPOSE) {
+    run(launch_transpose(P.dtype, c.W_r, c.wrt, P.H, P.E, st));
+    return err;
+  }
+  if (stage == MOE_BSTAGE_PLAN) return launch_plan(c.topk_idx, P.N, P.K, P.k, P.E, c.pb, st, nullptr, launches);
+
+  const ChunkGeom g = chunk_geom(P.N, P.K, P.k, i);
+  const int64_t R = (int64_t)P.k * g.n;
+  const RowsGeom rg = rows_geom(c.pb, P, i, R);
+  const int32_t* perm_i = c.pb.perm + g.pair_base;
+  const bool first = c.wg_init && i == 0;
+  switch (stage) {
+    case MOE_BSTAGE_RECOMPUTE:  // this chunk's expert intermediates a, u, h
+      if (c.fused) {
+        run(gemm_up_swiglu(P.dtype, rg, c.X, c.W_gate, c.W_up, c.h, c.a, c.u, P.H, P.F, st,
+                           perm_i, P.k, P.N));
+      } else {
+        run(launch_gather(P.dtype, c.X, c.xp, c.topk_idx, c.pb.pos, P.E, P.K, i, g.n, P.k, P.H,
+                          st));
+        run(gemm_up_swiglu(P.dtype, rg, c.xp, c.W_gate, c.W_up, c.h, c.a, c.u, P.H, P.F, st));
+      }
+      break;
+    case MOE_BSTAGE_DH:  // dh' = dYp W_down^T and the SwiGLU backward
+      // (bf16 reads the dY rows through perm; the gathered copy's buffer
+      // then only receives dXp)
+      if (!c.fused)
+        run(launch_gather(P.dtype, c.dY, c.o, c.topk_idx, c.pb.pos, P.E, P.K, i, g.n, P.k, P.H,
+                          st));
+      if (c.fused_swiglu) {
+        run(gemm_dh_swiglu(rg, c.fused ? c.dY : c.o, c.W_down, c.a, c.u, c.h, perm_i, c.gates,
+                           c.dgp, (int64_t)P.k * P.c_eff, P.N * P.k, P.H, P.F, st, P.k,
+                           c.fused ? P.N : 0));
+      } else {
+        run(gemm_dh(P.dtype, rg, c.o, c.W_down, c.dh, P.H, P.F, st));
+        run(launch_swiglu_bwd(P.dtype, c.dh, c.a, c.u, c.h, perm_i, c.gates, c.dg, R, P.F,
+                              P.N * P.k, st));
+      }
+      break;
+    case MOE_BSTAGE_WGRAD_DOWN:
+      run(gemm_wgrad_d(P.dtype, rg.offsets, c.h, c.fused ? c.dY : c.o, c.dW_down, P.E, P.H,
+                       P.F, st, first, c.fused ? perm_i : nullptr, P.k, P.N));
+      break;
+    case MOE_BSTAGE_WGRAD_GATE_UP:
+      run(gemm_wgrad_gu(P.dtype, rg.offsets, c.fused ? c.X : c.xp, c.a, c.u, c.dW_gate,
+                        c.dW_up, P.E, P.H, P.F, st, first, c.fused ? perm_i : nullptr, P.k,
+                        P.N));
+      break;
+    case MOE_BSTAGE_DX:
+      run(gemm_dx(P.dtype, rg, c.a, c.u, c.W_gate, c.W_up, c.o, P.H, P.F, st));
+      break;
+    case MOE_BSTAGE_COMBINE_BWD:
+      run(launch_combine_bwd(P.dtype, c.o, c.wrt, c.topk_idx, c.pb.pos, c.gates, c.dg, c.dX,
+                             c.dlogits, P.N, P.K, i, g.n, P.k, P.E, P.H, st,
+                             c.fused_swiglu ? c.dgp : nullptr,
+                             c.fused_swiglu ? dh_ntiles(rg, P.F) : 0, (int64_t)P.k * P.c_eff));
+      break;
+    case MOE_BSTAGE_DWR:
+      if (c.dW_r)
+        run(launch_dwr(P.dtype, c.X, perm_i, rg.offsets, c.dlogits, c.dW_r, P.k, P.E, P.H, P.N,
+                       st));
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return err;
+}
+
+}  // namespace
+}  // namespace moe
+
 MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const void* W_r,
                                  const void* W_gate, const void* W_up, const void* W_down,
                                  const void* dY, const int32_t* topk_idx, const float* gates,
@@ -277,82 +443,49 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
     return MOE_EINVAL;
   if (P.N > 0 && (uintptr_t)workspace % 256) return MOE_EINVAL;
   if (workspace_bytes < (size_t)P.bwd_workspace_bytes) return MOE_EWORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
   int launches = 0;
   (void)hipGetLastError();
-  const size_t wbytes = (size_t)P.E * P.H * P.F * sizeof(float);
-  // bf16: chunk 0's weight-gradient products store dW (zeros for experts
-  // without rows) and later chunks accumulate; fp32 accumulates from zero
-  const bool wg_init = P.dtype == MOE_BF16 && P.N > 0;
-  if (!wg_init) {
-    MOE_CHECK(launch_fill_zero(dW_gate, wbytes, st));
-    MOE_CHECK(launch_fill_zero(dW_up, wbytes, st));
-    MOE_CHECK(launch_fill_zero(dW_down, wbytes, st));
-  }
-  if (dW_r) MOE_CHECK(launch_fill_zero(dW_r, (size_t)P.H * P.E * sizeof(float), st));
+  const BwdCall c = bwd_call(P, X, W_r, W_gate, W_up, W_down, dY, topk_idx, gates, dX, dW_gate,
+                             dW_up, dW_down, dlogits, dgates, dW_r, workspace,
+                             (hipStream_t)stream);
+  if (bwd_stage(c, MOE_BSTAGE_ZERO, 0, &launches) != hipSuccess) return MOE_EHIP;
   if (P.N == 0) {
     fill_stats(stats, P, launches, 0, 0);
     return MOE_OK;
   }
-  const Layout L = make_layout(P, Pass::Backward, false, dgates == nullptr);
-  char* ws = (char*)workspace;
-  float* dg = dgates ? dgates : (float*)(ws + L.dgates);
-  void* wrt = ws + L.wrt;
-  MOE_CHECK(launch_transpose(P.dtype, W_r, wrt, P.H, P.E, st));
-  const PlanBuffers pb = plan_buffers(ws, L, nullptr, nullptr, nullptr);
-  if (launch_plan(topk_idx, P.N, P.K, P.k, P.E, pb, st, nullptr, &launches) != hipSuccess)
-    return MOE_EHIP;
-  void* xp = ws + L.xp;
-  void* o = ws + L.o;  // dXp (fp32 and the gathering path: the dY rows first)
-  void* h = ws + L.h;  // h, then g h
-  void* a = ws + L.a;  // a, then da
-  void* u = ws + L.u;  // u, then du
-  float* dh = (float*)(ws + L.dh);
-  float* dgp = (float*)(ws + L.dgp);
-  const bool fused_swiglu = P.dtype == MOE_BF16;
-  // bf16: the recompute, the dh GEMM and both weight gradients read the
-  // chunk's permuted rows of X and dY through perm (no gather, no Xp)
-  const bool fused = fused_gather_bwd(P);
-  for (int i = 0; i < P.K; ++i) {
-    const ChunkGeom g = chunk_geom(P.N, P.K, P.k, i);
-    const int64_t R = (int64_t)P.k * g.n;
-    const RowsGeom rg = rows_geom(pb, P, i, R);
-    const int32_t* perm_i = pb.perm + g.pair_base;
-    // recompute this chunk's expert intermediates
-    if (fused) {
-      MOE_CHECK(gemm_up_swiglu(P.dtype, rg, X, W_gate, W_up, h, a, u, P.H, P.F, st, perm_i, P.k,
-                               P.N));
-    } else {
-      MOE_CHECK(launch_gather(P.dtype, X, xp, topk_idx, pb.pos, P.E, P.K, i, g.n, P.k, P.H, st));
-      MOE_CHECK(gemm_up_swiglu(P.dtype, rg, xp, W_gate, W_up, h, a, u, P.H, P.F, st));
-    }
-    // backward through the chunk (bf16 reads the dY rows through perm; the
-    // gathered copy's buffer then only receives dXp)
-    if (!fused)
-      MOE_CHECK(launch_gather(P.dtype, dY, o, topk_idx, pb.pos, P.E, P.K, i, g.n, P.k, P.H, st));
-    if (fused_swiglu) {
-      MOE_CHECK(gemm_dh_swiglu(rg, fused ? dY : o, W_down, a, u, h, perm_i, gates, dgp,
-                               (int64_t)P.k * P.c_eff, P.N * P.k, P.H, P.F, st, P.k,
-                               fused ? P.N : 0));
-    } else {
-      MOE_CHECK(gemm_dh(P.dtype, rg, o, W_down, dh, P.H, P.F, st));
-      MOE_CHECK(launch_swiglu_bwd(P.dtype, dh, a, u, h, perm_i, gates, dg, R, P.F, P.N * P.k, st));
-    }
-    MOE_CHECK(gemm_wgrad_d(P.dtype, rg.offsets, h, fused ? dY : o, dW_down, P.E, P.H, P.F, st,
-                           wg_init && i == 0, fused ? perm_i : nullptr, P.k, P.N));
-    MOE_CHECK(gemm_wgrad_gu(P.dtype, rg.offsets, fused ? X : xp, a, u, dW_gate, dW_up, P.E, P.H,
-                            P.F, st, wg_init && i == 0, fused ? perm_i : nullptr, P.k, P.N));
-    MOE_CHECK(gemm_dx(P.dtype, rg, a, u, W_gate, W_up, o, P.H, P.F, st));
-    MOE_CHECK(launch_combine_bwd(P.dtype, o, wrt, topk_idx, pb.pos, gates, dg, dX, dlogits, P.N,
-                                 P.K, i, g.n, P.k, P.E, P.H, st, fused_swiglu ? dgp : nullptr,
-                                 fused_swiglu ? dh_ntiles(rg, P.F) : 0, (int64_t)P.k * P.c_eff));
-    if (dW_r)
-      MOE_CHECK(launch_dwr(P.dtype, X, perm_i, rg.offsets, dlogits, dW_r, P.k, P.E, P.H, P.N, st));
-  }
-  fill_stats(stats, P, launches, L.total,
-             (size_t)P.k * P.c_eff * P.F * (3 * elem_bytes(P.dtype) + (fused_swiglu ? 0 : 4)),
-             fused ? 1 : 2);
+  for (int s = MOE_BSTAGE_TRANSPOSE; s <= MOE_BSTAGE_PLAN; ++s)
+    if (bwd_stage(c, s, 0, &launches) != hipSuccess) return MOE_EHIP;
+  for (int i = 0; i < P.K; ++i)
+    for (int s = MOE_BSTAGE_RECOMPUTE; s <= MOE_BSTAGE_DWR; ++s)
+      if (bwd_stage(c, s, i, &launches) != hipSuccess) return MOE_EHIP;
+  fill_stats(stats, P, launches, c.L.total,
+             (size_t)P.k * P.c_eff * P.F * (3 * elem_bytes(P.dtype) + (c.fused_swiglu ? 0 : 4)),
+             c.fused ? 1 : 2);
   return MOE_OK;
+}
+
+MOE_API int moe_debug_stage_bwd(const moe_plan_t* plan, int32_t stage, int32_t chunk,
+                                const void* X, const void* W_r, const void* W_gate,
+                                const void* W_up, const void* W_down, const void* dY,
+                                const int32_t* topk_idx, const float* gates, void* dX,
+                                float* dW_gate, float* dW_up, float* dW_down, float* dlogits,
+                                float* dgates, float* dW_r, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!plan_ok(plan)) return MOE_EINVAL;
+  const moe_plan_t& P = *plan;
+  if (P.N == 0 || stage < MOE_BSTAGE_ZERO || stage > MOE_BSTAGE_DWR) return MOE_EINVAL;
+  if (stage >= MOE_BSTAGE_RECOMPUTE && (chunk < 0 || chunk >= P.K)) return MOE_EINVAL;
+  if (!X || !W_r || !W_gate || !W_up || !W_down || !dY || !topk_idx || !gates || !dX ||
+      !dW_gate || !dW_up || !dW_down || !dlogits || !workspace)
+    return MOE_EINVAL;
+  if ((uintptr_t)workspace % 256) return MOE_EINVAL;
+  if (workspace_bytes < (size_t)P.bwd_workspace_bytes) return MOE_EWORKSPACE;
+  int launches = 0;
+  (void)hipGetLastError();
+  const BwdCall c = bwd_call(P, X, W_r, W_gate, W_up, W_down, dY, topk_idx, gates, dX, dW_gate,
+                             dW_up, dW_down, dlogits, dgates, dW_r, workspace,
+                             (hipStream_t)stream);
+  return bwd_stage(c, stage, chunk, &launches) == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 MOE_API int moe_debug_topk(const float* logits, int64_t N, int32_t E, int32_t k,

@@ -133,6 +133,17 @@ struct Layout {
 enum class Pass { Forward, Backward, Debug };
 Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_dgates);
 
+// The forward call's argument checks (plan and required pointers; MOE_OK or
+// the status to return) and its launch sequence on a workspace of at least
+// make_layout(P, Pass::Forward, logits == nullptr, false).total bytes.
+int check_forward_args(const moe_plan_t* plan, const void* X, const void* W_r,
+                       const void* W_gate, const void* W_up, const void* W_down, const void* Y,
+                       const int32_t* topk_idx, const float* gates);
+int forward_impl(const moe_plan_t& P, const void* X, const void* W_r, const float* router_bias,
+                 const void* W_gate, const void* W_up, const void* W_down, void* Y,
+                 int32_t* topk_idx, float* gates, float* logits, void* workspace,
+                 hipStream_t st, moe_stats_t* stats);
+
 // ---- launchers (all asynchronous on `st`; return the first enqueue error)
 // With parts != nullptr the logits are first summed from the router's S
 // partials (s ascending), plus bias, and written to logits.

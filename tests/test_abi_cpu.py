@@ -24,7 +24,8 @@ def test_exports_every_declared_function():
     names = B.declared_functions()
     assert set(names) == {"moe_plan_chunks", "moe_bounded_forward", "moe_bounded_backward",
                           "moe_status_string", "moe_debug_topk", "moe_debug_plan",
-                          "moe_debug_stage", "cce_plan", "cce_forward", "cce_backward",
+                          "moe_debug_stage", "moe_debug_stage_bwd", "cce_plan", "cce_forward",
+                          "cce_backward",
                           "cce_debug_stage"}
     L = B.lib()
     for n in names:
@@ -163,6 +164,15 @@ def test_forward_argument_errors_before_any_launch():
     assert L.moe_debug_stage(ctypes.byref(p), 4, p.K, *ptrs[:9], fake, 1 << 30, None) == B.MOE_EINVAL
     assert L.moe_debug_topk(fake, 4, 8, 9, fake, fake, None) == B.MOE_EINVAL
     assert L.moe_debug_topk(fake, 4, 2048, 9, fake, fake, None) == B.MOE_EUNSUPPORTED
+    sb = [fake] * 15
+    assert L.moe_debug_stage_bwd(ctypes.byref(p), 5, 0, *sb, fake, p.bwd_workspace_bytes - 1,
+                                 None) == B.MOE_EWORKSPACE
+    assert L.moe_debug_stage_bwd(ctypes.byref(p), 10, 0, *sb, fake, 1 << 30, None) == B.MOE_EINVAL
+    assert L.moe_debug_stage_bwd(ctypes.byref(p), 5, p.K, *sb, fake, 1 << 30, None) == B.MOE_EINVAL
+    assert L.moe_debug_stage_bwd(ctypes.byref(bad), 5, 0, *sb, fake, 1 << 30, None) == B.MOE_EINVAL
+    sm = list(sb)
+    sm[5] = None  # dY
+    assert L.moe_debug_stage_bwd(ctypes.byref(p), 5, 0, *sm, fake, 1 << 30, None) == B.MOE_EINVAL
 
 
 
@@ -291,3 +301,18 @@ def test_cce_argument_errors_before_any_launch():
     p0 = B.cce_plan(0, 256, 5000, 1024)
     assert L.cce_forward(ctypes.byref(p0), *[None] * 5, None, 0, None) == B.MOE_OK
     assert L.cce_backward(ctypes.byref(p0), *[None] * 7, None, 0, None) == B.MOE_EINVAL
+
+
+def test_binding_argument_counts_match_the_headers():
+    """Every declared function's parameter count equals the number of
+    argument types the ctypes binding gives it (a miscount would pass
+    pointers in the wrong positions)."""
+    import re
+
+    L = B.lib()
+    for h in B.HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"\b((?:moe|cce)_[a-z_]+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S):
+            name, params = m.group(1), m.group(2).strip()
+            n = 0 if params in ("", "void") else params.count(",") + 1
+            assert len(getattr(L, name).argtypes) == n, (name, n)

@@ -187,11 +187,15 @@ def run_workload(name, full=True, wl=None, reduced=None):
             assert torch.equal(a, b_), key
         # weight gradients sum over tokens chunk by chunk: their last bits
         # depend on K, but every expert's (not only the sampled ones') must
-        # agree with the unchunked run to fp32 rounding
+        # agree with the unchunked run to fp32 rounding.  Two orders of an
+        # fp32 sum of n terms differ by about u sqrt(n) of its scale (the
+        # random-walk growth of rounding errors); n is the largest expert's
+        # row count, and the bound is never below 1e-5
+        order_tol = max(1e-5, 2 * 2.0 ** -24 * np.sqrt(counts.max()))
         for key in ("dW_gate", "dW_up", "dW_down", "dW_r"):
             dk = rel_err(dev_to_f64(out[key]), dev_to_f64(out1[key]))
-            say(f"[{name}]   {key} chunked vs unchunked {dk:.2e}")
-            assert dk <= 1e-5, key
+            say(f"[{name}]   {key} chunked vs unchunked {dk:.2e} (bound {order_tol:.2e})")
+            assert dk <= order_tol, key
         del out1
         # dW_r = X^T dlogits over the whole batch, against fp64 on the GPU's
         # dlogits (checked above on the sampled tokens): within the oracle

@@ -106,3 +106,35 @@ def test_plan_bit_exact(N, E, k, c, K_max):
         toks = oracle.chunk_tokens(N, K, i)
         got_pos = pos.reshape(N, k)[toks]
         assert np.array_equal(got_pos, ps_pos), i
+
+
+@pytest.mark.parametrize("name,n,c", [("tiny_f32", 256, 64), ("train_bf16", 777, 49)])
+def test_backward_stages_replay_the_call(name, n, c):
+    """moe_debug_stage_bwd: the whole-call stages and then every per-chunk
+    stage of chunks 0..K-1, in the backward call's order, rewrite the call's
+    outputs (first overwritten with garbage) bitwise."""
+    import datagen
+    from gpu_common import DevInputs, plan_for
+
+    require_lib()
+    wl = datagen.WORKLOADS[name]
+    inp = datagen.Inputs(wl.with_(N=n), dy=True)
+    d = DevInputs(inp)
+    plan = plan_for(wl, N=n, c=c)
+    say(f"backward stages {name} N={n} K={plan.K}")
+    _, idx, g, _, _ = B.moe_bounded_forward(plan, d.X, d.Wr, d.bias, d.Wg, d.Wu, d.Wd)
+    ws = B.workspace(plan, "bwd", DEV)
+    out = B.moe_bounded_backward(plan, d.X, d.Wr, d.Wg, d.Wu, d.Wd, d.dY, idx, g, ws=ws)
+    out.pop("stats")
+    torch.cuda.synchronize()
+    ref = {k_: v.clone() for k_, v in out.items()}
+    for v in out.values():
+        v.view(torch.uint8).fill_(0x7F)
+    for s in ("zero", "transpose", "plan"):
+        B.moe_debug_stage_bwd(plan, s, 0, d.X, d.Wr, d.Wg, d.Wu, d.Wd, d.dY, idx, g, out, ws)
+    for i in range(plan.K):
+        for s in ("recompute", "dh", "wgrad_down", "wgrad_gate_up", "dx", "combine_bwd", "dwr"):
+            B.moe_debug_stage_bwd(plan, s, i, d.X, d.Wr, d.Wg, d.Wu, d.Wd, d.dY, idx, g, out, ws)
+    torch.cuda.synchronize()
+    for k_, v in out.items():
+        assert torch.equal(v.view(torch.uint8), ref[k_].view(torch.uint8)), k_
