@@ -193,6 +193,33 @@ int moe_bounded_backward(const moe_plan_t* plan,
                          void* workspace, size_t workspace_bytes, void* stream,
                          moe_stats_t* stats);
 
+/*
+ * moe_bounded_forward_static -- moe_bounded_forward without a workspace
+ * argument, for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same inputs, outputs and results as moe_bounded_forward (bitwise: the
+ * same kernels run), but the per-call buffers live in a scratch array of
+ * MOE_STATIC_SCRATCH_BYTES bytes that the library holds on each GPU it runs
+ * on until the process ends.  The call allocates and frees nothing.
+ * Limit: the plan's forward layout must fit the array -- it is
+ * plan->fwd_workspace_bytes when logits is NULL (about N*E*4 bytes less when
+ * the caller passes logits); otherwise MOE_EWORKSPACE and nothing is
+ * enqueued.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (on different streams, or from different
+ * threads) race and give undefined results; calls in stream order are safe.
+ * The array keeps the last call's contents; the forward pass needs none of
+ * it cleared.
+ * Errors: as moe_bounded_forward; MOE_EWORKSPACE as above; MOE_EHIP also
+ *   when the runtime cannot give the array's device address.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int moe_bounded_forward_static(const moe_plan_t* plan,
+                               const void* X, const void* W_r, const float* router_bias,
+                               const void* W_gate, const void* W_up, const void* W_down,
+                               void* Y, int32_t* topk_idx, float* gates, float* logits,
+                               void* stream, moe_stats_t* stats);
+
 /* Static description of a status code; never NULL. */
 const char* moe_status_string(int status);
 

@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
     L.moe_bounded_forward.restype = _c.c_int
     L.moe_bounded_forward.argtypes = [_c.POINTER(MoePlan)] + [_vp] * 10 + [_vp, _c.c_size_t, _vp,
                                                                          _c.POINTER(MoeStats)]
+    L.moe_bounded_forward_static.restype = _c.c_int
+    L.moe_bounded_forward_static.argtypes = [_c.POINTER(MoePlan)] + [_vp] * 10 + [
+        _vp, _c.POINTER(MoeStats)]
     L.moe_bounded_backward.restype = _c.c_int
     L.moe_bounded_backward.argtypes = [_c.POINTER(MoePlan)] + [_vp] * 15 + [_vp, _c.c_size_t, _vp,
                                                                           _c.POINTER(MoeStats)]
@@ -217,6 +220,39 @@ def moe_bounded_forward(plan: MoePlan, X, W_r, router_bias, W_gate, W_up, W_down
         ctypes.byref(plan), _ptr(X), _ptr(W_r), _ptr(router_bias), _ptr(W_gate), _ptr(W_up),
         _ptr(W_down), _ptr(Y), _ptr(topk_idx), _ptr(gates), _ptr(logits), _ptr(ws),
         ws.numel(), _stream(dev, stream), ctypes.byref(st)), "moe_bounded_forward")
+    return Y, topk_idx, gates, logits, st.as_dict()
+
+
+def moe_bounded_forward_static(plan: MoePlan, X, W_r, router_bias, W_gate, W_up, W_down,
+                               Y=None, topk_idx=None, gates=None, logits=None,
+                               want_logits=True, stream=None):
+    """moe_bounded_forward on the library's static scratch array (no
+    workspace).  Returns (Y, topk_idx, gates, logits or None, stats dict)."""
+    dev = X.device
+    dt = torch_dtype(plan.dtype)
+    N, H, F, E, k = plan.N, plan.H, plan.F, plan.E, plan.k
+    _expect(X, "X", (N, H), dt, dev)
+    _expect(W_r, "W_r", (H, E), dt, dev)
+    if router_bias is not None:
+        _expect(router_bias, "router_bias", (E,), torch.float32, dev)
+    _expect(W_gate, "W_gate", (E, H, F), dt, dev)
+    _expect(W_up, "W_up", (E, H, F), dt, dev)
+    _expect(W_down, "W_down", (E, F, H), dt, dev)
+    Y = torch.empty((N, H), dtype=dt, device=dev) if Y is None else Y
+    topk_idx = torch.empty((N, k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    gates = torch.empty((N, k), dtype=torch.float32, device=dev) if gates is None else gates
+    if logits is None and want_logits:
+        logits = torch.empty((N, E), dtype=torch.float32, device=dev)
+    _expect(Y, "Y", (N, H), dt, dev)
+    _expect(topk_idx, "topk_idx", (N, k), torch.int32, dev)
+    _expect(gates, "gates", (N, k), torch.float32, dev)
+    if logits is not None:
+        _expect(logits, "logits", (N, E), torch.float32, dev)
+    st = MoeStats()
+    _check(lib().moe_bounded_forward_static(
+        ctypes.byref(plan), _ptr(X), _ptr(W_r), _ptr(router_bias), _ptr(W_gate), _ptr(W_up),
+        _ptr(W_down), _ptr(Y), _ptr(topk_idx), _ptr(gates), _ptr(logits),
+        _stream(dev, stream), ctypes.byref(st)), "moe_bounded_forward_static")
     return Y, topk_idx, gates, logits, st.as_dict()
 
 

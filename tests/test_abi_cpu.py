@@ -22,7 +22,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
 
 def test_exports_every_declared_function():
     names = B.declared_functions()
-    assert set(names) == {"moe_plan_chunks", "moe_bounded_forward", "moe_bounded_backward",
+    assert set(names) == {"moe_plan_chunks", "moe_bounded_forward", "moe_bounded_forward_static",
+                          "moe_bounded_backward",
                           "moe_status_string", "moe_debug_topk", "moe_debug_plan",
                           "moe_debug_stage", "moe_debug_stage_bwd", "cce_plan", "cce_forward",
                           "cce_backward",
@@ -316,3 +317,28 @@ def test_binding_argument_counts_match_the_headers():
             name, params = m.group(1), m.group(2).strip()
             n = 0 if params in ("", "void") else params.count(",") + 1
             assert len(getattr(L, name).argtypes) == n, (name, n)
+
+
+def test_static_forward_errors_before_any_launch():
+    """The static-scratch forward rejects a plan whose forward layout exceeds
+    MOE_STATIC_SCRATCH_BYTES, and bad arguments, on the host before it asks
+    for the scratch array's address or enqueues anything."""
+    import re
+
+    L = B.lib()
+    text = open(os.path.join(B.INCLUDE, "moebound.h")).read()
+    m = re.search(r"#define MOE_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    cap = int(m.group(1)) << int(m.group(2))
+    assert cap == 64 << 20
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced
+    ptrs = [fake] * 10
+    big = B.moe_plan_chunks(65536, 2048, 1024, 64, 8, 4096, 16, B.MOE_BF16)
+    assert big.fwd_workspace_bytes > cap
+    assert L.moe_bounded_forward_static(ctypes.byref(big), *ptrs, None, None) == B.MOE_EWORKSPACE
+    bad = B.MoePlan()
+    assert L.moe_bounded_forward_static(ctypes.byref(bad), *ptrs, None, None) == B.MOE_EINVAL
+    p = B.moe_plan_chunks(4096, 2048, 1408, 64, 8, 1024, 8, B.MOE_BF16)
+    assert p.fwd_workspace_bytes <= cap  # the balanced 4096-token forward fits
+    miss = list(ptrs)
+    miss[3] = None  # W_gate
+    assert L.moe_bounded_forward_static(ctypes.byref(p), *miss, None, None) == B.MOE_EINVAL
