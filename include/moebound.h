@@ -83,7 +83,7 @@ typedef struct moe_plan {
     int32_t H, F, E, k;          /* hidden, FFN width, experts, top-k         */
     int32_t c, K_max;            /* token budget per chunk, chunk cap         */
     int32_t K;                   /* eq. (1): min(ceil(N/c), K_max); 0 if N=0  */
-    int32_t reserved0;
+    int32_t flags;               /* MOE_PLAN_* options (moe_plan_set_flags)   */
     int64_t c_eff;               /* eq. (1): ceil(N/K); 0 if N = 0            */
     int64_t max_pairs_per_chunk; /* k * c_eff (route bound, E_p = 1)          */
     int64_t dispatch_bound_bytes;/* 2 * k * c_eff * H * b                     */
@@ -123,6 +123,34 @@ typedef struct moe_stats {
  */
 int moe_plan_chunks(int64_t N, int32_t H, int32_t F, int32_t E, int32_t k,
                     int32_t c, int32_t K_max, int32_t dtype, moe_plan_t* out);
+
+/*
+ * moe_plan_set_flags -- options of a plan; moe_plan_chunks leaves them 0.
+ *
+ * MOE_PLAN_EXACT_DW: order-invariant expert weight gradients.  [BSO]
+ *   (Summary, "Core principle"; Design Requirements 1-2) requires the chunked
+ *   run to reach exactly the unchunked values and gradients, with only the
+ *   order of computation changed.  By default dW_gate, dW_up and dW_down are
+ *   fp32 sums taken chunk by chunk, so their last bits depend on K.  With
+ *   this flag each operand of those sums -- X and dY per column h, and da, du
+ *   and g*h per expert and column f -- is first rounded to a power-of-two
+ *   grid fixed by that column's largest magnitude over the whole batch
+ *   (15-bit integers, |v| <= 2^14); the products are then summed exactly in
+ *   integers and rounded to fp32 once.  dW_gate, dW_up and dW_down are then
+ *   bitwise identical for every (c, K_max) of the same batch.  Cost: a first
+ *   pass over the chunks that recomputes a, u, h and runs the dh GEMM to find
+ *   the column maxima, the int8-digit weight-gradient products with a 64-bit
+ *   accumulator per weight element (workspace: 4 bytes per dW element beyond
+ *   dW itself, plus per-chunk digit planes), and one conversion pass.  The
+ *   other outputs are unchanged.  Needs dtype MOE_BF16, X and dY readable in
+ *   place (N*H*2 < 2^31, N*k*k < 2^32), c_eff <= 65536, H and F multiples of
+ *   128; else MOE_EUNSUPPORTED.  moe_debug_stage_bwd does not serve such plans.
+ * Updates plan->bwd_workspace_bytes.  Errors: MOE_EINVAL for a plan not from
+ *   moe_plan_chunks or an unknown flag; MOE_EUNSUPPORTED as above (the plan
+ *   is then unchanged).
+ */
+#define MOE_PLAN_EXACT_DW 1
+int moe_plan_set_flags(moe_plan_t* plan, int32_t flags);
 
 /*
  * moe_bounded_forward -- the layer's forward pass under the chunk schedule.
@@ -180,7 +208,9 @@ int moe_bounded_forward(const moe_plan_t* plan,
  *   dW_r [H][E] fp32 or NULL     X^T dlogits.
  * Per-token outputs (dX, dlogits, dgates) are bitwise independent of K.
  * Weight gradients sum over tokens chunk by chunk, so their last bits
- * depend on K; they are deterministic for a fixed plan.
+ * depend on K; they are deterministic for a fixed plan.  With
+ * MOE_PLAN_EXACT_DW (moe_plan_set_flags) dW_gate, dW_up and dW_down are
+ * bitwise independent of K as well.
  * workspace: at least plan->bwd_workspace_bytes bytes, 256-byte aligned.
  * Errors: as moe_bounded_forward, against bwd_workspace_bytes.
  */

@@ -38,7 +38,7 @@ class MoePlan(_c.Structure):
     _fields_ = [
         ("magic", _c.c_uint32), ("dtype", _c.c_int32), ("N", _c.c_int64),
         ("H", _c.c_int32), ("F", _c.c_int32), ("E", _c.c_int32), ("k", _c.c_int32),
-        ("c", _c.c_int32), ("K_max", _c.c_int32), ("K", _c.c_int32), ("reserved0", _c.c_int32),
+        ("c", _c.c_int32), ("K_max", _c.c_int32), ("K", _c.c_int32), ("flags", _c.c_int32),
         ("c_eff", _c.c_int64), ("max_pairs_per_chunk", _c.c_int64),
         ("dispatch_bound_bytes", _c.c_int64), ("fwd_workspace_bytes", _c.c_int64),
         ("bwd_workspace_bytes", _c.c_int64), ("debug_workspace_bytes", _c.c_int64),
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.moe_plan_chunks.restype = _c.c_int
     L.moe_plan_chunks.argtypes = [_c.c_int64, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
                                   _c.c_int32, _c.c_int32, _c.c_int32, _c.POINTER(MoePlan)]
+    L.moe_plan_set_flags.restype = _c.c_int
+    L.moe_plan_set_flags.argtypes = [_c.POINTER(MoePlan), _c.c_int32]
     L.moe_bounded_forward.restype = _c.c_int
     L.moe_bounded_forward.argtypes = [_c.POINTER(MoePlan)] + [_vp] * 10 + [_vp, _c.c_size_t, _vp,
                                                                          _c.POINTER(MoeStats)]
@@ -180,6 +182,16 @@ def moe_plan_chunks(N: int, H: int, F: int, E: int, k: int, c: int, K_max: int,
     plan = MoePlan()
     _check(lib().moe_plan_chunks(N, H, F, E, k, c, K_max, dtype, ctypes.byref(plan)),
            "moe_plan_chunks")
+    return plan
+
+
+MOE_PLAN_EXACT_DW = 1
+
+
+def moe_plan_set_flags(plan: MoePlan, flags: int) -> MoePlan:
+    """Set the plan's options in place (MOE_PLAN_EXACT_DW: order-invariant
+    expert weight gradients); returns the plan."""
+    _check(lib().moe_plan_set_flags(ctypes.byref(plan), flags), "moe_plan_set_flags")
     return plan
 
 

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoebound.so")
 
 SOURCES = ["api.hip", "route.hip", "plan.hip", "dispatch.hip", "gemm_fwd.hip", "gemm_bwd.hip",
-           "cce.hip", "gemm_cce.hip", "noalloc.hip"]
+           "cce.hip", "gemm_cce.hip", "noalloc.hip", "exact_dw.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

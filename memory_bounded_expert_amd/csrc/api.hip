@@ -71,6 +71,13 @@ Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_d
         L.dh = take(rows * F * 4);
       L.wrt = take(E * H * b);
       if (need_dgates) L.dgates = take(N * k * 4);
+      if (p.flags & MOE_PLAN_EXACT_DW) {
+        L.ldk = exact_ldk(p);
+        L.cmax = take((2 * H + 3 * E * F) * 4);
+        L.offpad = take((E + 1) * 4);
+        L.planes = take(2 * (2 * H + 3 * F) * (size_t)L.ldk);
+        L.acc_hi = take(3 * E * H * F * 4);
+      }
     }
   }
   L.total = cur;
@@ -268,6 +275,14 @@ int forward_impl(const moe_plan_t& P, const void* X, const void* W_r, const floa
 
 }  // namespace moe
 
+MOE_API int moe_plan_set_flags(moe_plan_t* plan, int32_t flags) {
+  if (!plan_ok(plan) || (flags & ~MOE_PLAN_EXACT_DW)) return MOE_EINVAL;
+  if ((flags & MOE_PLAN_EXACT_DW) && !exact_dw_ok(*plan)) return MOE_EUNSUPPORTED;
+  plan->flags = flags;
+  plan->bwd_workspace_bytes = (int64_t)make_layout(*plan, Pass::Backward, false, true).total;
+  return MOE_OK;
+}
+
 MOE_API int moe_bounded_forward(const moe_plan_t* plan, const void* X, const void* W_r,
                                 const float* router_bias, const void* W_gate, const void* W_up,
                                 const void* W_down, void* Y, int32_t* topk_idx, float* gates,
@@ -304,6 +319,20 @@ struct BwdCall {
   bool fused;         // bf16: permuted rows of X and dY read through perm
   bool fused_swiglu;  // bf16: SwiGLU backward in the dh GEMM's epilogue
   bool wg_init;       // bf16: chunk 0 stores dW instead of accumulating
+  bool exact;         // MOE_PLAN_EXACT_DW: order-invariant weight gradients
+  uint32_t *xmax, *dymax, *amax, *umax, *hmax;  // exact: column maxima
+  int32_t* offpad;
+  int8_t* plane[10];  // exact: hi/lo digit planes of X, dY, da, du, g h
+  int32_t* acc_hi[3]; // exact: high words of the dW_gate, dW_up, dW_down accumulators
+};
+
+// Backward stages that only the order-invariant weight gradients run (after
+// the public enum moe_bwd_stage's).
+enum {
+  kBStageExactZero = 100,  // zero the column maxima
+  kBStageColmaxXY,         // column maxima of X and dY over the batch
+  kBStageColmaxRows,       // per chunk: column maxima of da, du, g h per expert
+  kBStageFinalize          // accumulators to fp32 dW
 };
 
 BwdCall bwd_call(const moe_plan_t& P, const void* X, const void* W_r, const void* W_gate,
@@ -332,6 +361,26 @@ BwdCall bwd_call(const moe_plan_t& P, const void* X, const void* W_r, const void
   c.fused_swiglu = P.dtype == MOE_BF16;
   c.fused = fused_gather_bwd(P);
   c.wg_init = P.dtype == MOE_BF16 && P.N > 0;
+  c.exact = (P.flags & MOE_PLAN_EXACT_DW) != 0;
+  if (c.exact) {
+    const int64_t H = P.H, F = P.F, E = P.E, ldk = c.L.ldk;
+    uint32_t* cm = (uint32_t*)(ws + c.L.cmax);
+    c.xmax = cm;
+    c.dymax = cm + H;
+    c.amax = cm + 2 * H;
+    c.umax = c.amax + E * F;
+    c.hmax = c.umax + E * F;
+    c.offpad = (int32_t*)(ws + c.L.offpad);
+    int8_t* pl = (int8_t*)(ws + c.L.planes);
+    const int64_t cols[5] = {H, H, F, F, F};
+    for (int z = 0; z < 5; ++z) {
+      c.plane[2 * z] = pl;
+      c.plane[2 * z + 1] = pl + cols[z] * ldk;
+      pl += 2 * cols[z] * ldk;
+    }
+    int32_t* ah = (int32_t*)(ws + c.L.acc_hi);
+    for (int w = 0; w < 3; ++w) c.acc_hi[w] = ah + (int64_t)w * E * H * F;
+  }
   return c;
 }
 
@@ -363,6 +412,26 @@ hipError_t bwd_stage(const BwdCall& c, int stage, int i, int* launches) {
     run(launch_transpose(P.dtype, c.W_r, c.wrt, P.H, P.E, st));
     return err;
   }
+  if (stage == kBStageExactZero) {
+    run(launch_fill_zero(c.xmax, (2 * (size_t)P.H + 3 * (size_t)P.E * P.F) * 4, st));
+    return err;
+  }
+  if (stage == kBStageColmaxXY) {
+    run(launch_colmax(c.X, P.N, P.H, c.xmax, st));
+    run(launch_colmax(c.dY, P.N, P.H, c.dymax, st));
+    return err;
+  }
+  if (stage == kBStageFinalize) {
+    // dW_gate, dW_up: A = X (per column h), B = da, du (per expert and f);
+    // dW_down: A = g h (per expert and f), B = dY (per column h)
+    run(launch_exact_finalize(c.dW_gate, c.acc_hi[0], c.xmax, false, c.amax, true, P.E, P.H,
+                              P.F, st));
+    run(launch_exact_finalize(c.dW_up, c.acc_hi[1], c.xmax, false, c.umax, true, P.E, P.H, P.F,
+                              st));
+    run(launch_exact_finalize(c.dW_down, c.acc_hi[2], c.hmax, true, c.dymax, false, P.E, P.F,
+                              P.H, st));
+    return err;
+  }
   if (stage == MOE_BSTAGE_PLAN) return launch_plan(c.topk_idx, P.N, P.K, P.k, P.E, c.pb, st, nullptr, launches);
 
   const ChunkGeom g = chunk_geom(P.N, P.K, P.k, i);
@@ -370,6 +439,42 @@ hipError_t bwd_stage(const BwdCall& c, int stage, int i, int* launches) {
   const RowsGeom rg = rows_geom(c.pb, P, i, R);
   const int32_t* perm_i = c.pb.perm + g.pair_base;
   const bool first = c.wg_init && i == 0;
+  if (c.exact && (stage == MOE_BSTAGE_WGRAD_DOWN || stage == MOE_BSTAGE_WGRAD_GATE_UP)) {
+    // order-invariant weight gradients: WGRAD_DOWN writes the chunk's digit
+    // planes and runs the down product, WGRAD_GATE_UP the other two
+    const int64_t ldk = c.L.ldk;
+    uint32_t* lo_g = reinterpret_cast<uint32_t*>(c.dW_gate);
+    uint32_t* lo_u = reinterpret_cast<uint32_t*>(c.dW_up);
+    uint32_t* lo_d = reinterpret_cast<uint32_t*>(c.dW_down);
+    const bool init = i == 0;
+    if (stage == MOE_BSTAGE_WGRAD_DOWN) {
+      ExactChunk x;
+      x.X = DigitPlanesSrc{c.X, P.H, P.H, perm_i, P.k, c.xmax, 0, c.plane[0], c.plane[1]};
+      x.dY = DigitPlanesSrc{c.dY, P.H, P.H, perm_i, P.k, c.dymax, 0, c.plane[2], c.plane[3]};
+      x.da = DigitPlanesSrc{c.a, P.F, P.F, nullptr, 1, c.amax, 1, c.plane[4], c.plane[5]};
+      x.du = DigitPlanesSrc{c.u, P.F, P.F, nullptr, 1, c.umax, 1, c.plane[6], c.plane[7]};
+      x.hg = DigitPlanesSrc{c.h, P.F, P.F, nullptr, 1, c.hmax, 1, c.plane[8], c.plane[9]};
+      x.offsets = rg.offsets;
+      x.offpad = c.offpad;
+      x.E = P.E;
+      x.ldk = ldk;
+      if (launch_digitize(x, st) != hipSuccess) return hipErrorLaunchFailure;
+      *launches += 2;
+      run(launch_exact_wgrad(c.plane[8], c.plane[9], c.plane[2], c.plane[3], ldk, rg.offsets,
+                             c.offpad, lo_d, c.acc_hi[2], P.E, P.F, P.H, init, st));
+    } else {
+      run(launch_exact_wgrad(c.plane[0], c.plane[1], c.plane[4], c.plane[5], ldk, rg.offsets,
+                             c.offpad, lo_g, c.acc_hi[0], P.E, P.H, P.F, init, st));
+      run(launch_exact_wgrad(c.plane[0], c.plane[1], c.plane[6], c.plane[7], ldk, rg.offsets,
+                             c.offpad, lo_u, c.acc_hi[1], P.E, P.H, P.F, init, st));
+    }
+    return err;
+  }
+  if (stage == kBStageColmaxRows) {
+    run(launch_colmax_rows(c.a, c.u, c.h, rg.offsets, P.E, P.F, (int64_t)P.k * P.c_eff, c.amax,
+                           c.umax, c.hmax, st));
+    return err;
+  }
   switch (stage) {
     case MOE_BSTAGE_RECOMPUTE:  // this chunk's expert intermediates a, u, h
       if (c.fused) {
@@ -455,9 +560,19 @@ MOE_API int moe_bounded_backward(const moe_plan_t* plan, const void* X, const vo
   }
   for (int s = MOE_BSTAGE_TRANSPOSE; s <= MOE_BSTAGE_PLAN; ++s)
     if (bwd_stage(c, s, 0, &launches) != hipSuccess) return MOE_EHIP;
+  if (c.exact) {
+    // first pass: the column maxima that fix every operand's grid (whole
+    // batch, so the same for every chunking)
+    for (int s : {(int)kBStageExactZero, (int)kBStageColmaxXY})
+      if (bwd_stage(c, s, 0, &launches) != hipSuccess) return MOE_EHIP;
+    for (int i = 0; i < P.K; ++i)
+      for (int s : {(int)MOE_BSTAGE_RECOMPUTE, (int)MOE_BSTAGE_DH, (int)kBStageColmaxRows})
+        if (bwd_stage(c, s, i, &launches) != hipSuccess) return MOE_EHIP;
+  }
   for (int i = 0; i < P.K; ++i)
     for (int s = MOE_BSTAGE_RECOMPUTE; s <= MOE_BSTAGE_DWR; ++s)
       if (bwd_stage(c, s, i, &launches) != hipSuccess) return MOE_EHIP;
+  if (c.exact && bwd_stage(c, kBStageFinalize, 0, &launches) != hipSuccess) return MOE_EHIP;
   fill_stats(stats, P, launches, c.L.total,
              (size_t)P.k * P.c_eff * P.F * (3 * elem_bytes(P.dtype) + (c.fused_swiglu ? 0 : 4)),
              c.fused ? 1 : 2);
@@ -474,6 +589,7 @@ MOE_API int moe_debug_stage_bwd(const moe_plan_t* plan, int32_t stage, int32_t c
   if (!plan_ok(plan)) return MOE_EINVAL;
   const moe_plan_t& P = *plan;
   if (P.N == 0 || stage < MOE_BSTAGE_ZERO || stage > MOE_BSTAGE_DWR) return MOE_EINVAL;
+  if (P.flags & MOE_PLAN_EXACT_DW) return MOE_EUNSUPPORTED;
   if (stage >= MOE_BSTAGE_RECOMPUTE && (chunk < 0 || chunk >= P.K)) return MOE_EINVAL;
   if (!X || !W_r || !W_gate || !W_up || !W_down || !dY || !topk_idx || !gates || !dX ||
       !dW_gate || !dW_up || !dW_down || !dlogits || !workspace)

@@ -74,6 +74,17 @@ inline bool fused_gather_bwd(const moe_plan_t& p) {
   return fused_gather(p) && indexed_rows_ok(p.N, p.k);
 }
 
+// Order-invariant weight gradients (MOE_PLAN_EXACT_DW): padded rows of a
+// chunk's digit planes (each expert segment rounded up to 64 rows).
+inline int64_t exact_ldk(const moe_plan_t& p) {
+  return ((int64_t)p.k * p.c_eff + 64 * (int64_t)p.E + 63) / 64 * 64;
+}
+inline bool exact_dw_ok(const moe_plan_t& p) {
+  return p.dtype == MOE_BF16 && p.H % 128 == 0 && p.F % 128 == 0 && p.c_eff <= 65536 &&
+         (p.N == 0 || fused_gather_bwd(p)) &&
+         (int64_t)(p.H > p.F ? p.H : p.F) * exact_ldk(p) < ((int64_t)1 << 31);
+}
+
 // Upper bound on the row-grouped GEMM's M-tiles of T rows for a chunk of R
 // pairs: sum_e ceil(M_e / T) <= R / T + (number of non-empty experts).
 inline int64_t max_row_tiles(int64_t R, int E, int T) {
@@ -123,12 +134,62 @@ struct Layout {
   size_t dgp = 0;         // [F/64][k c_eff] f32 backward, bf16: dgate shares per N-tile
   size_t wrt = 0;         // [E][H] backward: W_r transposed
   size_t dgates = 0;      // [N*k] f32 backward, when the caller passes none
+  // backward with MOE_PLAN_EXACT_DW (exact_dw.hip):
+  size_t cmax = 0;        // u32 column maxima: X [H], dY [H], da, du, g h [E][F] each
+  size_t offpad = 0;      // [E+1] i32 padded segment starts of the current chunk
+  size_t planes = 0;      // int8 digit planes [C][ldk]: X, dY (C = H), da, du, g h (C = F), hi and lo
+  size_t acc_hi = 0;      // [3][E][H][F] i32 high words of the dW_gate, dW_up, dW_down accumulators
+  int64_t ldk = 0;        // padded rows per digit plane
   size_t total = 0;
   int64_t nblk = 0;
   int64_t max_tiles = 0;
   int row_tile = kRowTile;
   bool split = false;     // small_tiles / small_count present
 };
+
+// ---- order-invariant weight gradients (exact_dw.hip)
+// Column maxima of |x| as fp32 bit patterns (atomicMax into zeroed arrays):
+// over all N rows of a bf16 [N][C] matrix ...
+hipError_t launch_colmax(const void* src, int64_t N, int C, uint32_t* out, hipStream_t st);
+// ... and per expert over a chunk's expert-sorted rows of three bf16 [R][C]
+// buffers (segments offsets[e] .. offsets[e+1], at most max_rows rows).
+hipError_t launch_colmax_rows(const void* a, const void* u, const void* h, const int32_t* offsets,
+                              int E, int C, int64_t max_rows, uint32_t* amax, uint32_t* umax,
+                              uint32_t* hmax, hipStream_t st);
+// One matrix whose chunk rows become digit planes: row r of the chunk is
+// source row rows[r] / row_div (or r itself without rows) of src.
+struct DigitPlanesSrc {
+  const void* src;
+  int64_t ld;
+  int C;
+  const int32_t* rows;
+  int row_div;
+  const uint32_t* cmax;  // [C], or [E][C] with per_expert
+  int per_expert;
+  int8_t* hi;            // [C][ldk]
+  int8_t* lo;
+};
+struct ExactChunk {
+  DigitPlanesSrc X, dY, da, du, hg;
+  const int32_t* offsets;  // the chunk's [E+1] segments
+  int32_t* offpad;         // [E+1] written: padded segment starts
+  int E;
+  int64_t ldk;
+};
+// The chunk's padded segment starts, then the digit planes of all five.
+hipError_t launch_digitize(const ExactChunk& x, hipStream_t st);
+// acc64[e][m][n] (init: =, else +=) sum over expert e's chunk rows of
+// vA[m][k] vB[n][k], from digit planes; the 64-bit accumulator is split into
+// c_lo (low words) and c_hi.  M % 128 == 0, N % 64 == 0.
+hipError_t launch_exact_wgrad(const int8_t* a_hi, const int8_t* a_lo, const int8_t* b_hi,
+                              const int8_t* b_lo, int64_t ldk, const int32_t* offsets,
+                              const int32_t* offpad, uint32_t* c_lo, int32_t* c_hi, int E, int M,
+                              int N, bool init, hipStream_t st);
+// dw[e][m][n] = acc64 * 2^((eA_m - 14) + (eB_n - 14)), rounded once to fp32,
+// in place over the low words in dw.
+hipError_t launch_exact_finalize(float* dw, const int32_t* c_hi, const uint32_t* amax,
+                                 bool a_per_expert, const uint32_t* bmax, bool b_per_expert, int E,
+                                 int M, int N, hipStream_t st);
 
 enum class Pass { Forward, Backward, Debug };
 Layout make_layout(const moe_plan_t& p, Pass pass, bool need_logits, bool need_dgates);

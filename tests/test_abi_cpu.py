@@ -22,7 +22,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
 
 def test_exports_every_declared_function():
     names = B.declared_functions()
-    assert set(names) == {"moe_plan_chunks", "moe_bounded_forward", "moe_bounded_forward_static",
+    assert set(names) == {"moe_plan_chunks", "moe_plan_set_flags", "moe_bounded_forward",
+                          "moe_bounded_forward_static",
                           "moe_bounded_backward",
                           "moe_status_string", "moe_debug_topk", "moe_debug_plan",
                           "moe_debug_stage", "moe_debug_stage_bwd", "cce_plan", "cce_forward",
@@ -47,7 +48,8 @@ def test_struct_layout_matches_c():
 int main(void) {
   printf("plan %zu\nstats %zu\ncce %zu\n", sizeof(moe_plan_t), sizeof(moe_stats_t),
          sizeof(cce_plan_t));
-  O(moe_plan_t, N) O(moe_plan_t, K) O(moe_plan_t, c_eff) O(moe_plan_t, debug_workspace_bytes)
+  O(moe_plan_t, N) O(moe_plan_t, K) O(moe_plan_t, flags) O(moe_plan_t, c_eff)
+  O(moe_plan_t, debug_workspace_bytes)
   O(moe_stats_t, c_eff) O(moe_stats_t, workspace_bytes)
   O(cce_plan_t, V) O(cce_plan_t, H) O(cce_plan_t, S) O(cce_plan_t, strip_bound_bytes)
   O(cce_plan_t, bwd_workspace_bytes)
@@ -64,7 +66,7 @@ int main(void) {
                                                               text=True).stdout.splitlines())
     assert int(lines["plan"]) == ctypes.sizeof(B.MoePlan)
     assert int(lines["stats"]) == ctypes.sizeof(B.MoeStats)
-    for f in ("N", "K", "c_eff", "debug_workspace_bytes"):
+    for f in ("N", "K", "flags", "c_eff", "debug_workspace_bytes"):
         assert int(lines[f"moe_plan_t.{f}"]) == getattr(B.MoePlan, f).offset
     for f in ("c_eff", "workspace_bytes"):
         assert int(lines[f"moe_stats_t.{f}"]) == getattr(B.MoeStats, f).offset
@@ -342,3 +344,41 @@ def test_static_forward_errors_before_any_launch():
     miss = list(ptrs)
     miss[3] = None  # W_gate
     assert L.moe_bounded_forward_static(ctypes.byref(p), *miss, None, None) == B.MOE_EINVAL
+
+
+def test_plan_set_flags():
+    """MOE_PLAN_EXACT_DW: accepted for bf16 plans whose X and dY are read in
+    place and c_eff <= 65536 (the backward workspace grows by the column
+    maxima, the digit planes and the high words of the accumulators);
+    refused otherwise, leaving the plan unchanged."""
+    N, H, F, E, k = 65536, 2048, 1024, 64, 8
+    p = B.moe_plan_chunks(N, H, F, E, k, 4096, 16, B.MOE_BF16)
+    base = p.bwd_workspace_bytes
+    B.moe_plan_set_flags(p, B.MOE_PLAN_EXACT_DW)
+    assert p.flags == B.MOE_PLAN_EXACT_DW
+    ldk = -(-(k * p.c_eff + 64 * E) // 64) * 64
+    extra = p.bwd_workspace_bytes - base
+    need = (2 * H + 3 * E * F) * 4 + (E + 1) * 4 + 2 * (2 * H + 3 * F) * ldk + 3 * E * H * F * 4
+    assert need <= extra <= need + 4 * 256
+    B.moe_plan_set_flags(p, 0)
+    assert p.flags == 0 and p.bwd_workspace_bytes == base
+    # refusals: unknown flag, fp32, c_eff above 65536, a plan not from moe_plan_chunks
+    with pytest.raises(B.MoeError) as e1:
+        B.moe_plan_set_flags(p, 2)
+    assert e1.value.status == B.MOE_EINVAL
+    f32 = B.moe_plan_chunks(256, 64, 128, 8, 2, 64, 8, B.MOE_F32)
+    with pytest.raises(B.MoeError) as e2:
+        B.moe_plan_set_flags(f32, B.MOE_PLAN_EXACT_DW)
+    assert e2.value.status == B.MOE_EUNSUPPORTED and f32.flags == 0
+    wide = B.moe_plan_chunks(70000, 256, 256, 8, 2, 70000, 1, B.MOE_BF16)
+    with pytest.raises(B.MoeError) as e3:
+        B.moe_plan_set_flags(wide, B.MOE_PLAN_EXACT_DW)
+    assert e3.value.status == B.MOE_EUNSUPPORTED
+    with pytest.raises(B.MoeError) as e4:
+        B.moe_plan_set_flags(B.MoePlan(), B.MOE_PLAN_EXACT_DW)
+    assert e4.value.status == B.MOE_EINVAL
+    # the backward's debug stages do not serve such plans
+    B.moe_plan_set_flags(p, B.MOE_PLAN_EXACT_DW)
+    fake = ctypes.c_void_p(0x100000)
+    assert B.lib().moe_debug_stage_bwd(ctypes.byref(p), 5, 0, *[fake] * 15, fake, 1 << 40,
+                                       None) == B.MOE_EUNSUPPORTED
