@@ -481,6 +481,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="forward-only workloads: also time forward+backward steps (reported "
                          "under forward_backward); a forward+backward workload always does")
+    ap.add_argument("--exact-dw", action="store_true",
+                    help="also time the backward with order-invariant weight gradients "
+                         "(plan flag MOE_PLAN_EXACT_DW; reported under forward_backward.exact_dw)")
     ap.add_argument("--blas-yardstick", action="store_true",
                     help="also time the vendor library's batched GEMM (torch.bmm) on one chunk's "
                          "expert products with equal, contiguous row groups (reported under "
@@ -753,6 +756,40 @@ def main():
                                else ref_g[k_])
             assert same, f"backward stage re-launches changed {k_}"
         del ref_g
+
+        if args.exact_dw and bf:
+            # the opt-in order-invariant weight gradients: the same step with
+            # the plan flag (a first pass over the chunks finds the column
+            # maxima; int8-digit products into 64-bit accumulators)
+            pe = B.moe_plan_chunks(wl.N, wl.H, wl.F, wl.E, wl.k, wl.c, wl.K_max, plan.dtype)
+            B.moe_plan_set_flags(pe, B.MOE_PLAN_EXACT_DW)
+            wse = B.workspace(pe, "bwd", dev)
+            gx = {k_: torch.empty_like(v_) for k_, v_ in grads.items()}
+
+            def xstep():
+                return B.moe_bounded_backward(pe, X, Wr, Wg, Wu, Wd, dY, idx, gates, ws=wse,
+                                              stream=stream, **gx)
+
+            for _ in range(max(1, args.warmup)):
+                xstep()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                xstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_x = e0.elapsed_time(e1) / args.steps
+            for k_ in ("dX", "dlogits", "dgates", "dW_r"):  # unchanged by the flag
+                a_, b2 = gx[k_], grads[k_]
+                if a_.dtype == torch.bfloat16:
+                    a_, b2 = a_.view(torch.int16), b2.view(torch.int16)
+                assert torch.equal(a_, b2), f"exact-dW backward changed {k_}"
+            fb["exact_dw"] = {"backward_ms": round(ms_x, 4),
+                              "vs_default_backward": round(ms_x / ms_b, 3),
+                              "workspace_bytes": pe.bwd_workspace_bytes}
+            log(f"exact-dW backward: {ms_x:.3f} ms ({ms_x / ms_b:.2f}x the default), workspace "
+                f"{pe.bwd_workspace_bytes} B")
+            del wse, gx
 
     p1 = B.moe_plan_chunks(wl.N, wl.H, wl.F, wl.E, wl.k, wl.c, 1, plan.dtype)
     step_ms = fb["ms_per_step"] if train else ms

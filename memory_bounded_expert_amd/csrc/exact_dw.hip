@@ -252,6 +252,7 @@ constexpr int kXBM = 128, kXBN = 64, kXBK = 64;  // tile; K-tile in bytes (int8 
 constexpr int kXNS = 3;                           // LDS stages
 constexpr int kXStage = (2 * kXBM + 2 * kXBN) * kXBK;
 constexpr int kXPT = 6;                           // loads per thread per K-tile
+static_assert(4 * 64 * 36 * 8 <= kXNS * kXStage, "epilogue staging must fit the stages");
 
 __global__ __launch_bounds__(kThreads, 2) void exact_wgrad_kernel(const ExactParams p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -345,23 +346,51 @@ __global__ __launch_bounds__(kThreads, 2) void exact_wgrad_kernel(const ExactPar
     gemm::wait_vmcnt<0>();
   }
 
-  // exact partial 2^16 hh + 2^8 (hl + lh) + ll, added into the 64-bit
-  // accumulator (lane: rows 4 lg + q of fragment row i, column l16)
+  // exact partial 2^16 hh + 2^8 (hl + lh) + ll (lane: rows 4 lg + q of
+  // fragment row i, column l16), parked in this wave's share of the freed
+  // stages (64 rows of 32 values, rows padded to 36 so the four row groups
+  // of a write land in distinct banks), then added into the 64-bit
+  // accumulator four columns at a time: 16-byte, row-contiguous accesses to
+  // the low and high words, all of a lane's old values requested first
+  constexpr int kLd = 36;
+  gemm::lds_barrier();  // every wave is done with the operand stages
+  int64_t* stg = reinterpret_cast<int64_t*>(smem + wave * (64 * kLd * 8));
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * 64 + i * 16 + 4 * lg + q;
-        const int n = n0 + wn * 32 + j * 16 + l16;
-        const int64_t idx = ((int64_t)e * p.M + m) * p.N + n;
-        int64_t v = ((int64_t)acc[0][i][j][q] << 16) + ((int64_t)acc[1][i][j][q] << 8) +
-                    (int64_t)acc[2][i][j][q];
-        if (!p.init) v += (int64_t)(((uint64_t)(uint32_t)p.c_hi[idx] << 32) | p.c_lo[idx]);
-        p.c_lo[idx] = (uint32_t)(uint64_t)v;
-        p.c_hi[idx] = (int32_t)(v >> 32);
-      }
+      for (int q = 0; q < 4; ++q)
+        stg[(i * 16 + 4 * lg + q) * kLd + j * 16 + l16] =
+            ((int64_t)acc[0][i][j][q] << 16) + ((int64_t)acc[1][i][j][q] << 8) +
+            (int64_t)acc[2][i][j][q];
+  gemm::wave_lds_sync();
+  constexpr int kIt = 64 * 32 / 4 / 64;  // 4-column pieces per lane
+  int64_t base[kIt];
+  u32x4_t olo[kIt], ohi[kIt];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int item = lane + 64 * it, r = item >> 3, c4 = (item & 7) * 4;
+    base[it] = ((int64_t)e * p.M + m0 + wm * 64 + r) * p.N + n0 + wn * 32 + c4;
+    if (!p.init) {
+      olo[it] = *reinterpret_cast<const u32x4_t*>(p.c_lo + base[it]);
+      ohi[it] = *reinterpret_cast<const u32x4_t*>(p.c_hi + base[it]);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int item = lane + 64 * it, r = item >> 3, c4 = (item & 7) * 4;
+    u32x4_t lo, hi;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int64_t v = stg[r * kLd + c4 + c];
+      if (!p.init) v += (int64_t)(((uint64_t)ohi[it][c] << 32) | olo[it][c]);
+      lo[c] = (uint32_t)(uint64_t)v;
+      hi[c] = (uint32_t)(uint64_t)(v >> 32);
+    }
+    *reinterpret_cast<u32x4_t*>(p.c_lo + base[it]) = lo;
+    *reinterpret_cast<u32x4_t*>(p.c_hi + base[it]) = hi;
+  }
 }
 
 // ---- accumulators to fp32 in place: dW = acc 2^((eA - 14) + (eB - 14)),
