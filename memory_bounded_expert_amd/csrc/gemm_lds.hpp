@@ -621,6 +621,28 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
     const int row = m0 + wm * WM + lane;
     if (p.row_scale && lane < WM && row < row_end) row_scale_lane = p.row_scale[row];
   }
+  // The SwiGLU backward's row gates (two dependent loads: the row's pair,
+  // then its gate), likewise requested before the pipeline: the epilogue's
+  // thread t handles rows slab*SR + t/G8 + it*(THREADS/G8) of the tile, so
+  // a wave's threads touch BM/WAVES distinct rows; lane q of the wave holds
+  // the gate of the wave's q-th row (order: slab, iteration, row within the
+  // wave's group).
+  float sw_gate_lane = 0.f;
+  if constexpr (MODE == Mode::Rows && EPI == Epi::SwiGLUBwd) {
+    constexpr int G8 = BN / 8, RPW = 64 / G8, RSTEP = C::THREADS / G8;
+    static_assert(64 % G8 == 0 && C::THREADS % G8 == 0 && BM / C::WAVES <= 64, "gate table");
+    constexpr int SLAB_FIT = (NS * C::STAGE) / (WM * (BN + 4) * 4);
+    constexpr int SLAB = SLAB_FIT >= S::WGM ? S::WGM : (SLAB_FIT >= 2 && S::WGM % 2 == 0 ? 2 : 1);
+    constexpr int SR = SLAB * WM, ITEMS = SR * G8 / C::THREADS;
+    if (lane < BM / C::WAVES) {
+      const int j = lane % RPW, it = (lane / RPW) % ITEMS, sl = lane / (RPW * ITEMS);
+      const int row = m0 + sl * SR + wave * RPW + j + it * RSTEP;
+      if (row < row_end) {
+        const int32_t pr = p.sw_perm[row];
+        if ((uint64_t)pr < (uint64_t)p.sw_nk) sw_gate_lane = p.sw_gates[pr];
+      }
+    }
+  }
 
   // ---- pipeline.  NS stages; tile t goes to stage t % NS.  The prologue
   // fills every stage and reads tile 0's fragments.  Iteration kt then
@@ -812,6 +834,11 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
     T* Ca = static_cast<T*>(p.C2);
     T* Cu = static_cast<T*>(p.C3);
     float* dgp = p.sw_dgp + (int64_t)(n0 / BN) * p.sw_rows;
+    // thread t: 8 columns c of rows t/G8 + it*RSTEP of each slab; all of a
+    // slab's a, u, h pieces are requested before the first is used, and the
+    // gates come from the table loaded before the pipeline
+    constexpr int RPW = 64 / G8, RSTEP = C::THREADS / G8, ITEMS = SR * G8 / C::THREADS;
+    const int c = tid % G8, rt = tid / G8;
 #pragma unroll
     for (int sl = 0; sl < S::WGM / SLAB; ++sl) {
       lds_barrier();  // previous users of the LDS are done
@@ -825,12 +852,29 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
             for (int q = 0; q < 4; ++q)
               stg[(r0 + i * 16 + 4 * lg + q) * LD + wn * WN + j * 16 + l16] = acc[0][i][j][q];
       }
-      lds_barrier();
       const int row0 = m0 + sl * SR;
-      for (int idx = tid; idx < SR * G8; idx += C::THREADS) {
-        const int r = idx / G8, c = idx - r * G8;
-        const int grow = row0 + r;
-        const bool ok = grow < row_end;
+      u32x4_t va[ITEMS], vu[ITEMS], vh[ITEMS];
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int grow = row0 + rt + it * RSTEP;
+        if (grow < row_end) {
+          const int64_t o = (int64_t)grow * p.ldc + n0 + c * 8;
+          va[it] = *reinterpret_cast<const u32x4_t*>(Ca + o);
+          vu[it] = *reinterpret_cast<const u32x4_t*>(Cu + o);
+          vh[it] = *reinterpret_cast<const u32x4_t*>(Ch + o);
+        }
+      }
+      lds_barrier();
+      // results overwrite the loaded pieces in registers; every store of
+      // the slab goes out after the last computation, so no store waits on
+      // another piece's loads
+      float parts[ITEMS];
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int r = rt + it * RSTEP;
+        const bool ok = row0 + r < row_end;
+        // this row's gate: table entry (sl, it, row within the wave's group)
+        const float g = __shfl(sw_gate_lane, (sl * ITEMS + it) * RPW + (rt % RPW), 64);
         float part = 0.f;
         if (ok) {
           float dv[8], av[8], uv[8], hv[8];
@@ -841,12 +885,9 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
             dv[q] = d0[q];
             dv[q + 4] = d1[q];
           }
-          const int32_t pr = p.sw_perm[grow];
-          const float g = (uint64_t)pr < (uint64_t)p.sw_nk ? p.sw_gates[pr] : 0.f;
-          const int64_t o = (int64_t)grow * p.ldc + n0 + c * 8;
-          unpack16(*reinterpret_cast<const u32x4_t*>(Ca + o), av, T());
-          unpack16(*reinterpret_cast<const u32x4_t*>(Cu + o), uv, T());
-          unpack16(*reinterpret_cast<const u32x4_t*>(Ch + o), hv, T());
+          unpack16(va[it], av, T());
+          unpack16(vu[it], uv, T());
+          unpack16(vh[it], hv, T());
           float da[8], du[8], hg[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
@@ -857,13 +898,28 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
             du[q] = d * av[q] * sa;
             hg[q] = g * hv[q];
           }
-          *reinterpret_cast<u32x4_t*>(Ca + o) = pack16(da, T());
-          *reinterpret_cast<u32x4_t*>(Cu + o) = pack16(du, T());
-          *reinterpret_cast<u32x4_t*>(Ch + o) = pack16(hg, T());
+          va[it] = pack16(da, T());
+          vu[it] = pack16(du, T());
+          vh[it] = pack16(hg, T());
+        } else {
+          // (never stored; defined on every path so that the stores below
+          // do not wait on the loads that target these registers)
+          va[it] = vu[it] = vh[it] = u32x4_t{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int m = 1; m < G8; m <<= 1) part += __shfl_xor(part, m);
-        if (ok && c == 0) dgp[grow] = part;
+        parts[it] = part;
+      }
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int grow = row0 + rt + it * RSTEP;
+        if (grow < row_end) {
+          const int64_t o = (int64_t)grow * p.ldc + n0 + c * 8;
+          *reinterpret_cast<u32x4_t*>(Ca + o) = va[it];
+          *reinterpret_cast<u32x4_t*>(Cu + o) = vu[it];
+          *reinterpret_cast<u32x4_t*>(Ch + o) = vh[it];
+          if (c == 0) dgp[grow] = parts[it];
+        }
       }
     }
     return;
