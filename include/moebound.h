@@ -336,7 +336,12 @@ int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk,
  *   MOE_BSTAGE_DWR          dW_r += X^T dlogits over the chunk's tokens
  *                           (nothing when dW_r is NULL).
  * (fp32 plans, and bf16 plans whose X or dY cannot be read in place, also
- * run the gather of X rows in RECOMPUTE and of dY rows in DH.)
+ * run the gather of X rows in RECOMPUTE and of dY rows in DH.  bf16 plans
+ * whose chunks take the 256-row GEMM tiles -- experts averaging at least 96
+ * rows per chunk, H and F multiples of 128 -- compute a, u and h inside the
+ * DH stage's kernel, which keeps them on chip: their RECOMPUTE stage only
+ * gathers, if anything.)  The dgate shares are per 128 columns of F (64 when
+ * F is not a multiple of 128) and summed in one order whatever the tiles.
  * Precondition: the last call that used `workspace` was moe_bounded_backward
  * with the same plan and arguments (dgates and dW_r NULL or not as there).
  * Running ZERO, TRANSPOSE, PLAN and then RECOMPUTE .. DWR for chunks

@@ -318,6 +318,7 @@ struct BwdCall {
   float *dh, *dgp;
   bool fused;         // bf16: permuted rows of X and dY read through perm
   bool fused_swiglu;  // bf16: SwiGLU backward in the dh GEMM's epilogue
+  bool fused_rdh;     // bf16, 256-row tiles: recompute inside the dh kernel
   bool wg_init;       // bf16: chunk 0 stores dW instead of accumulating
   bool exact;         // MOE_PLAN_EXACT_DW: order-invariant weight gradients
   uint32_t *xmax, *dymax, *amax, *umax, *hmax;  // exact: column maxima
@@ -359,6 +360,7 @@ BwdCall bwd_call(const moe_plan_t& P, const void* X, const void* W_r, const void
   c.dh = (float*)(ws + c.L.dh);
   c.dgp = (float*)(ws + c.L.dgp);
   c.fused_swiglu = P.dtype == MOE_BF16;
+  c.fused_rdh = fused_recompute_dh(P);
   c.fused = fused_gather_bwd(P);
   c.wg_init = P.dtype == MOE_BF16 && P.N > 0;
   c.exact = (P.flags & MOE_PLAN_EXACT_DW) != 0;
@@ -477,7 +479,13 @@ hipError_t bwd_stage(const BwdCall& c, int stage, int i, int* launches) {
   }
   switch (stage) {
     case MOE_BSTAGE_RECOMPUTE:  // this chunk's expert intermediates a, u, h
-      if (c.fused) {
+      if (c.fused_rdh) {
+        // computed inside the dh stage's kernel; only the X rows' gather
+        // (when they are not read through perm) happens here
+        if (!c.fused)
+          run(launch_gather(P.dtype, c.X, c.xp, c.topk_idx, c.pb.pos, P.E, P.K, i, g.n, P.k, P.H,
+                            st));
+      } else if (c.fused) {
         run(gemm_up_swiglu(P.dtype, rg, c.X, c.W_gate, c.W_up, c.h, c.a, c.u, P.H, P.F, st,
                            perm_i, P.k, P.N));
       } else {
@@ -492,7 +500,12 @@ hipError_t bwd_stage(const BwdCall& c, int stage, int i, int* launches) {
       if (!c.fused)
         run(launch_gather(P.dtype, c.dY, c.o, c.topk_idx, c.pb.pos, P.E, P.K, i, g.n, P.k, P.H,
                           st));
-      if (c.fused_swiglu) {
+      if (c.fused_rdh) {
+        run(gemm_recompute_dh(rg, c.fused ? c.X : c.xp, c.fused ? c.dY : c.o, c.W_gate, c.W_up,
+                              c.W_down, c.a, c.u, c.h, perm_i, c.gates, c.dgp,
+                              (int64_t)P.k * P.c_eff, P.N * P.k, P.H, P.F, st, P.k,
+                              c.fused ? P.N : 0));
+      } else if (c.fused_swiglu) {
         run(gemm_dh_swiglu(rg, c.fused ? c.dY : c.o, c.W_down, c.a, c.u, c.h, perm_i, c.gates,
                            c.dgp, (int64_t)P.k * P.c_eff, P.N * P.k, P.H, P.F, st, P.k,
                            c.fused ? P.N : 0));

@@ -1,5 +1,6 @@
 // Backward contractions: dY W_down^T, [da du] [W_gate W_up]^T, and the
 // per-expert weight gradients accumulated chunk by chunk.
+#include "gemm_fused_bwd.hpp"
 #include "gemm_kernel.hpp"
 #include "gemm_lds.hpp"
 
@@ -111,8 +112,12 @@ hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd
   return dtype == MOE_BF16 ? dh_bf16(p, grid, bn, g.row_tile, st) : dh_t<float>(p, grid, bn, st);
 }
 
+// The dgate shares are per 128 columns of F (64 when F is not a multiple of
+// 128), whatever the row tiles, so that chunkings whose chunks take different
+// tile shapes (or the fused recompute + dh kernel) sum them alike.
 int dh_ntiles(const RowsGeom& g, int F) {
-  return F / (g.row_tile == kRowTileLarge ? (F % 256 == 0 ? 256 : 128) : pick_bn(F, true));
+  (void)g;
+  return F / (F % kFusedDhTile == 0 ? kFusedDhTile : 64);
 }
 
 hipError_t gemm_dh_swiglu(const RowsGeom& g, const void* dYp, const void* Wd, void* a_da,
@@ -135,6 +140,30 @@ hipError_t gemm_dh_swiglu(const RowsGeom& g, const void* dYp, const void* Wd, vo
   const int bn = F / p.ntiles;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
   return dh_swiglu_bf16(p, grid, bn, g.row_tile, st);
+}
+
+hipError_t gemm_recompute_dh(const RowsGeom& g, const void* Xp, const void* dYp, const void* Wg,
+                             const void* Wu, const void* Wd, void* a_da, void* u_du, void* h_hg,
+                             const int32_t* perm, const float* gates, float* dgp, int64_t rows,
+                             int64_t Nk, int H, int F, hipStream_t st, int k, int64_t x_rows) {
+  if (g.grid_m == 0) return hipSuccess;
+  if (g.row_tile != kRowTileLarge || F % kFusedDhTile != 0 || H % 128 != 0) return hipErrorInvalidValue;
+  static_assert(FusedBwdShape::BN == kFusedDhTile && FusedBwdShape::BM == kRowTileLarge, "tile");
+  FusedBwdParams p{};
+  p.X = Xp; p.dY = dYp; p.lda = H;
+  if (x_rows > 0) {  // row r of the chunk is row perm[r] / k of X and of dY
+    if (k < 1) return hipErrorInvalidValue;
+    p.a_rows = perm; p.a_row_div = k; p.a_src_rows = x_rows;
+  }
+  p.Wg = Wg; p.Wu = Wu; p.Wd = Wd;
+  p.H = H; p.F = F;
+  p.h_hg = h_hg; p.a_da = a_da; p.u_du = u_du;
+  p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
+  p.ntiles = F / kFusedDhTile;
+  p.perm = perm; p.gates = gates; p.nk = Nk;
+  p.dgp = dgp; p.dgp_rows = rows;
+  const dim3 grid((unsigned)(g.grid_m * p.ntiles));
+  return launch_fused_bwd<FusedBwdShape>(p, grid, st);
 }
 
 hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du, const void* Wg,

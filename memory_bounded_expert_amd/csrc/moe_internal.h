@@ -109,6 +109,12 @@ inline bool split_tiles(const moe_plan_t& p) {
   return p.dtype == MOE_BF16 && row_tile_for(p) == kRowTileLarge;
 }
 
+// The bf16 backward with kRowTileLarge tiles runs a chunk's recompute and
+// dh products as one kernel (a, u, h stay in registers; 128-column tiles of F).
+inline bool fused_recompute_dh(const moe_plan_t& p) {
+  return p.dtype == MOE_BF16 && row_tile_for(p) == kRowTileLarge;
+}
+
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct Layout {
   size_t logits = 0;      // [N][E] f32, forward only, when the caller passes none
@@ -292,7 +298,8 @@ hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd
                    int F, hipStream_t st);
 // bf16: dh' = dYp W_down[e]^T with the SwiGLU backward in the epilogue (as
 // launch_swiglu_bwd, dh' never stored): da, du, g h over a, u, h; the per
-// N-tile shares of dgate into dgp [dh_ntiles][rows].
+// N-tile shares of dgate into dgp [dh_ntiles][rows] (N-tiles of 128 columns,
+// 64 when F is not a multiple of 128).
 int dh_ntiles(const RowsGeom& g, int F);
 // With x_rows > 0, dYp is not a buffer: row r of the chunk is row perm[r] / k
 // of the x_rows-row dY, read straight from it.
@@ -300,6 +307,17 @@ hipError_t gemm_dh_swiglu(const RowsGeom& g, const void* dYp, const void* Wd, vo
                           void* u_du, void* h_hg, const int32_t* perm, const float* gates,
                           float* dgp, int64_t rows, int64_t Nk, int H, int F, hipStream_t st,
                           int k = 1, int64_t x_rows = 0);
+// bf16, kRowTileLarge geometry: a = Xp W_gate[e], u = Xp W_up[e], h =
+// silu(a) u (kept in registers, rounded to bf16), then dh' = dYp W_down[e]^T
+// and the SwiGLU backward as gemm_dh_swiglu's, in one kernel: da, du and g h
+// into a_da, u_du, h_hg, and the per 128-column tile shares of dgate into
+// dgp [F / 128][rows].  With x_rows > 0 row r of the chunk is row perm[r] / k
+// of X and dY (x_rows rows each); otherwise Xp and dYp are the chunk's rows.
+hipError_t gemm_recompute_dh(const RowsGeom& g, const void* Xp, const void* dYp, const void* Wg,
+                             const void* Wu, const void* Wd, void* a_da, void* u_du, void* h_hg,
+                             const int32_t* perm, const float* gates, float* dgp, int64_t rows,
+                             int64_t Nk, int H, int F, hipStream_t st, int k, int64_t x_rows);
+constexpr int kFusedDhTile = 128;  // columns of F per tile of gemm_recompute_dh
 // dXp = da W_gate[e]^T + du W_up[e]^T
 hipError_t gemm_dx(int dtype, const RowsGeom& g, const void* da, const void* du, const void* Wg,
                    const void* Wu, void* dXp, int H, int F, hipStream_t st);

@@ -8,7 +8,9 @@ through the C ABI, against the full fp64 oracle (forward and backward):
   * k = 1 (every gate exactly 1; the backward's row-indexed loads then take
     a pair index as its token, with no division);
   * one token per chunk (c = 1, K = N);
-  * K_max binding: c = 10 asks for 100 chunks, K_max = 3 gives c_eff = 334;
+  * K_max binding: c = 10 asks for 100 chunks, K_max = 3 gives c_eff = 334
+    (with F = 256 also: chunked and unchunked runs on different tile shapes
+    and backward kernels);
   * every token routed to the same two experts (a Zipf(12) router bias over
     8 experts with top-2): two full segments per chunk, six empty experts;
   * the largest k: k = E = 64, every token in every expert;
@@ -52,6 +54,12 @@ CASES = {
     # K_max binds: K = 3 chunks of 334, 333, 333 tokens
     "kmax_binds_bf16": BF.with_(name="kmax_binds_bf16", N=1000, H=128, E=16, k=4, F=128, c=10,
                                 K_max=3),
+    # the same with F = 256: the K = 3 chunks (83 rows per expert) take the
+    # 128-row tiles and the two-kernel backward, the unchunked run (250 rows
+    # per expert) the 256-row tiles and the fused recompute + dh kernel; the
+    # dgate shares must still be summed alike
+    "mixed_tiles_bf16": BF.with_(name="mixed_tiles_bf16", N=1000, H=128, E=16, k=4, F=256, c=10,
+                                 K_max=3),
     # all routing on two experts: segments of a whole chunk, the rest empty
     "two_hot_experts_bf16": BF.with_(name="two_hot_experts_bf16", N=600, H=128, E=8, k=2, F=128,
                                      c=300, K_max=4, zipf_s=12.0),
