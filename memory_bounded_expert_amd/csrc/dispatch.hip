@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
   }
 }
 
-template <typename T>
+template <typename T, int COLS>
 __global__ __launch_bounds__(kThreads) void dwr_kernel(const T* __restrict__ X,
                                                        const int32_t* __restrict__ perm,
                                                        const int32_t* __restrict__ offsets,
@@ -268,15 +268,21 @@ __global__ __launch_bounds__(kThreads) void dwr_kernel(const T* __restrict__ X,
   // itself: each token is read by its k experts' work-groups, from cache
   // after the first); rows of other experts would add
   // dlogits[t, e] = 0 exactly, so they are skipped.  One work-group per
-  // (64-wide column block of H, expert): CPB threads cover a row's 64 values
-  // with 16-byte loads and RG row groups stride the expert's segment (rows
-  // ascending per thread); the groups' partial sums are then added in group
-  // order, so the result does not depend on timing.
+  // (COLS-wide column block of H, expert).  The expert's segment goes in
+  // blocks of kThreads rows: the block's tokens and dlogits are staged in LDS
+  // first (one load each per thread), then CPB threads cover a row's COLS
+  // values with 16-byte loads, RG row groups taking every RG-th row
+  // (ascending per thread) with UNR rows' loads in flight.  The groups'
+  // partial sums are added in group order at the end, so the result does not
+  // depend on timing.
   constexpr int EPC = Elem<T>::kPer16B;
-  constexpr int COLS = 64;
   constexpr int CPB = COLS / EPC;
+  static_assert(COLS % EPC == 0 && kThreads % CPB == 0 && COLS <= kThreads, "column block");
   constexpr int RG = kThreads / CPB;
+  constexpr int UNR = 4;
   __shared__ float part[RG][COLS + 1];
+  __shared__ int64_t tok[kThreads];
+  __shared__ float dl[kThreads];
   const int e = blockIdx.y;
   const int cb = blockIdx.x;
   const int cg = threadIdx.x % CPB, rg = threadIdx.x / CPB;
@@ -286,26 +292,37 @@ __global__ __launch_bounds__(kThreads) void dwr_kernel(const T* __restrict__ X,
   float acc[EPC];
 #pragma unroll
   for (int q = 0; q < EPC; ++q) acc[q] = 0.f;
-  auto row = [&](int r, float& d, float* v) __attribute__((always_inline)) {
-    const int64_t t = perm[r] / k;
-    d = (uint64_t)t < (uint64_t)N ? dlogits[t * E + e] : 0.f;  // t >= N only on a corrupt plan
-    unpack16(*reinterpret_cast<const u32x4_t*>(X + ((uint64_t)t < (uint64_t)N ? t : 0) * H + col), v, T());
-  };
-  int r = r0 + rg;
-  for (; r + 3 * RG < r1; r += 4 * RG) {
-    float d[4], v[4][EPC];
+  for (int b0 = r0; b0 < r1; b0 += kThreads) {
+    const int nb = min(kThreads, r1 - b0);
+    __syncthreads();  // the previous block's rows are consumed
+    if ((int)threadIdx.x < nb) {
+      const int64_t t = perm[b0 + threadIdx.x] / k;
+      const bool ok = (uint64_t)t < (uint64_t)N;  // t >= N only on a corrupt plan
+      tok[threadIdx.x] = ok ? t : 0;
+      dl[threadIdx.x] = ok ? dlogits[t * E + e] : 0.f;
+    }
+    __syncthreads();
+    int j = rg;
+    for (; j + (UNR - 1) * RG < nb; j += UNR * RG) {
+      u32x4_t v[UNR];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) row(r + j * RG, d[j], v[j]);
+      for (int u = 0; u < UNR; ++u) v[u] = *reinterpret_cast<const u32x4_t*>(X + tok[j + u * RG] * H + col);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int u = 0; u < UNR; ++u) {
+        float x[EPC];
+        unpack16(v[u], x, T());
+        const float d = dl[j + u * RG];
 #pragma unroll
-      for (int q = 0; q < EPC; ++q) acc[q] = fmaf(d[j], v[j][q], acc[q]);
-  }
-  for (; r < r1; r += RG) {
-    float d, v[EPC];
-    row(r, d, v);
+        for (int q = 0; q < EPC; ++q) acc[q] = fmaf(d, x[q], acc[q]);
+      }
+    }
+    for (; j < nb; j += RG) {
+      float x[EPC];
+      unpack16(*reinterpret_cast<const u32x4_t*>(X + tok[j] * H + col), x, T());
+      const float d = dl[j];
 #pragma unroll
-    for (int q = 0; q < EPC; ++q) acc[q] = fmaf(d, v[q], acc[q]);
+      for (int q = 0; q < EPC; ++q) acc[q] = fmaf(d, x[q], acc[q]);
+    }
   }
 #pragma unroll
   for (int q = 0; q < EPC; ++q) part[rg][cg * EPC + q] = acc[q];
@@ -409,14 +426,21 @@ hipError_t launch_combine_bwd(int dtype, const void* dXp, const void* WrT, const
 hipError_t launch_dwr(int dtype, const void* X, const int32_t* perm, const int32_t* offsets,
                       const float* dlogits, float* dWr, int k, int E, int H, int64_t N,
                       hipStream_t st) {
-  // H is a multiple of 64 (checked when the plan is made)
-  const dim3 grid((unsigned)(H / 64), (unsigned)E);
-  if (dtype == MOE_BF16)
-    dwr_kernel<bf16_t><<<grid, kThreads, 0, st>>>((const bf16_t*)X, perm, offsets, dlogits, dWr, k,
-                                                  E, H, N);
-  else
-    dwr_kernel<float><<<grid, kThreads, 0, st>>>((const float*)X, perm, offsets, dlogits, dWr, k,
-                                                 E, H, N);
+  // column blocks of 256, 128 or 64 (the widest dividing H; H is a
+  // multiple of 64, checked when the plan is made; fp32 at most 128)
+  const int cols = (dtype == MOE_BF16 && H % 256 == 0) ? 256 : (H % 128 == 0 ? 128 : 64);
+  if (H % 64 != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(H / cols), (unsigned)E);
+  if (dtype == MOE_BF16) {
+    const bf16_t* x = (const bf16_t*)X;
+    if (cols == 256) dwr_kernel<bf16_t, 256><<<grid, kThreads, 0, st>>>(x, perm, offsets, dlogits, dWr, k, E, H, N);
+    else if (cols == 128) dwr_kernel<bf16_t, 128><<<grid, kThreads, 0, st>>>(x, perm, offsets, dlogits, dWr, k, E, H, N);
+    else dwr_kernel<bf16_t, 64><<<grid, kThreads, 0, st>>>(x, perm, offsets, dlogits, dWr, k, E, H, N);
+  } else {
+    const float* x = (const float*)X;
+    if (cols == 128) dwr_kernel<float, 128><<<grid, kThreads, 0, st>>>(x, perm, offsets, dlogits, dWr, k, E, H, N);
+    else dwr_kernel<float, 64><<<grid, kThreads, 0, st>>>(x, perm, offsets, dlogits, dWr, k, E, H, N);
+  }
   return hipGetLastError();
 }
 
