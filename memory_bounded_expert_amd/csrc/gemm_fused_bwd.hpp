@@ -88,14 +88,11 @@ __attribute__((amdgpu_waves_per_eu(S::WGM * S::WGN / 4))) void fused_bwd_kernel(
   const int total = *p.tile_count * p.ntiles;
   const int bid = (int)blockIdx.x;
   if (bid >= total) return;
-  const int lid = xcd_contiguous(bid, total);
-  const int mt = lid / p.ntiles;
-  const int nt = lid - mt * p.ntiles;
-  const int2 tl = p.tiles[mt];
-  const int e = __builtin_amdgcn_readfirstlane(tl.x);
-  const int m0 = __builtin_amdgcn_readfirstlane(tl.y);
-  const int n0 = __builtin_amdgcn_readfirstlane(nt * BN);
-  const int row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+  const RowsTile t = rows_tile(p.tiles, p.offsets, xcd_contiguous(bid, total), p.ntiles, BM);
+  const int e = __builtin_amdgcn_readfirstlane(t.e);
+  const int m0 = __builtin_amdgcn_readfirstlane(t.m0);
+  const int n0 = __builtin_amdgcn_readfirstlane(t.nt * BN);
+  const int row_end = __builtin_amdgcn_readfirstlane(t.row_end);
   const int64_t rows = (int64_t)min(row_end - m0, BM);
 
   // A rows: this lane's source-row byte offsets (the same for X and dY)
@@ -480,7 +477,7 @@ __attribute__((amdgpu_waves_per_eu(S::WGM * S::WGN / 4))) void fused_bwd_kernel(
       for (int m = 1; m < G8; m <<= 1) part += __shfl_xor(part, m);
       if (m0 + tr < row_end) {
         *reinterpret_cast<u32x4_t*>(Chg + (int64_t)(m0 + tr) * p.F + n0 + c * 8) = pack16(hg, T());
-        if (c == 0) p.dgp[(int64_t)nt * p.dgp_rows + m0 + tr] = part;
+        if (c == 0) p.dgp[(int64_t)(n0 / BN) * p.dgp_rows + m0 + tr] = part;
       }
     }
   }

@@ -193,6 +193,28 @@ __device__ __forceinline__ int xcd_contiguous(int L, int total) {
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+// The (expert, rows, N-tile) tile that renumbered id lid of a row-grouped
+// grid computes.  An expert's M-tiles are consecutive in the tile list and
+// start at offsets[e] + i * bm, so its ids are the range [first * ntiles,
+// (first + me) * ntiles); inside that range they run N-tile major, M-tile
+// minor.  The me work-groups that read one slice of the expert's weights
+// then have adjacent ids, so they run at the same time on one XCD and share
+// the slice in its L2, and the ntiles work-groups that read one M-tile's
+// rows lie within me * ntiles ids of each other.
+struct RowsTile {
+  int e, m0, nt, row_end;
+};
+__device__ __forceinline__ RowsTile rows_tile(const int2* tiles, const int32_t* offsets, int lid,
+                                              int ntiles, int bm) {
+  const int mtg = lid / ntiles;
+  const int2 tl = tiles[mtg];
+  const int seg0 = offsets[tl.x], seg1 = offsets[tl.x + 1];
+  const int me = (seg1 - seg0 + bm - 1) / bm;
+  const int local = lid - (mtg - (tl.y - seg0) / bm) * ntiles;
+  const int nt = local / me;
+  return RowsTile{tl.x, seg0 + (local - nt * me) * bm, nt, seg1};
+}
+
 // Weight-gradient grids are (M-tiles, N-tiles, experts).  The tiles of one
 // expert all read that expert's activation rows, so they go to one XCD (the
 // renumbered ids run expert by expert) and the rows are fetched into one L2

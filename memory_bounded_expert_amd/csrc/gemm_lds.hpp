@@ -258,16 +258,15 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   int64_t k_begin = 0;
   int k_len = p.K;
   if constexpr (MODE == Mode::Rows) {
-    // XCD-aware renumbering of the 1-D grid (xcd_contiguous)
+    // XCD-aware renumbering of the 1-D grid (xcd_contiguous), then the
+    // expert-local N-major order of rows_tile
     const int total = *p.tile_count * p.ntiles;
     if (bid >= total) return;
-    const int lid = xcd_contiguous(bid, total);
-    const int mt = lid / p.ntiles;
-    n0 = (lid - mt * p.ntiles) * BN;
-    const int2 tl = p.tiles[mt];
-    e = tl.x;
-    m0 = tl.y;
-    row_end = p.offsets[e + 1];
+    const RowsTile t = rows_tile(p.tiles, p.offsets, xcd_contiguous(bid, total), p.ntiles, BM);
+    e = t.e;
+    m0 = t.m0;
+    n0 = t.nt * BN;
+    row_end = t.row_end;
   } else if constexpr (MODE == Mode::Dense) {
     // blockIdx.z: K slice of a split product (slice z covers
     // [z * Kseg, (z + 1) * Kseg) and writes the z-th partial output)
