@@ -712,7 +712,9 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
     // is old + new in one fp32 add.  The operand stages are free once every
     // wave's last fragment reads are done (the barrier); after it each wave
     // touches only its own share.  Rows past row_end are neither read nor
-    // written.
+    // written.  C is read and written once per launch, so its accesses are
+    // marked non-temporal: they then do not evict the operand rows that the
+    // expert's other tiles read from L2.
     using AG = AccGeom<S, C>;
     float* stg = reinterpret_cast<float*>(smem + wave * AG::PWB);
     const int rw0 = m0 + wm * WM, cw0 = n0 + wn * WN;  // this wave's block
@@ -731,7 +733,7 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
     if (accumulate) {
 #pragma unroll
       for (int u = 0; u < AG::PER; ++u)
-        if (grow(0, u) < row_end) old[0][u] = *gptr(0, u);
+        if (grow(0, u) < row_end) old[0][u] = __builtin_nontemporal_load(gptr(0, u));
     }
     lds_barrier();  // every wave's last fragment reads are done
 #pragma unroll
@@ -748,13 +750,13 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
       if (accumulate && s + 1 < AG::NSUB) {
 #pragma unroll
         for (int u = 0; u < AG::PER; ++u)
-          if (grow(s + 1, u) < row_end) old[(s + 1) & 1][u] = *gptr(s + 1, u);
+          if (grow(s + 1, u) < row_end) old[(s + 1) & 1][u] = __builtin_nontemporal_load(gptr(s + 1, u));
       }
 #pragma unroll
       for (int u = 0; u < AG::PER; ++u) {
         const int idx = lane + u * 64, r = idx / AG::VW, c4 = idx - r * AG::VW;
         const f32x4_t add = *reinterpret_cast<const f32x4_t*>(stg + r * AG::LD + c4 * 4);
-        if (grow(s, u) < row_end) *gptr(s, u) = accumulate ? old[s & 1][u] + add : add;
+        if (grow(s, u) < row_end) __builtin_nontemporal_store(accumulate ? old[s & 1][u] + add : add, gptr(s, u));
       }
       wave_lds_sync();  // this slice's reads are done before the next slice's writes
     }
