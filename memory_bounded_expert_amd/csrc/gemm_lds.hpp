@@ -79,6 +79,22 @@ __device__ __forceinline__ void lds_load16(const i32x4_t& srd, void* lds, uint32
                : "memory", "m0");
 }
 
+// The same with the LDS destination as a 32-bit LDS address (no conversion
+// of a generic pointer per load)
+__device__ __forceinline__ void lds_load16_at(const i32x4_t& srd, uint32_t lds_addr, uint32_t voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  // (a resource chosen by a wave-uniform condition: kept in scalar registers)
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(srd.x);
+  r.y = __builtin_amdgcn_readfirstlane(srd.y);
+  r.z = __builtin_amdgcn_readfirstlane(srd.z);
+  r.w = __builtin_amdgcn_readfirstlane(srd.w);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
 // 4 bytes per lane from a buffer straight into LDS at lds + 4 * lane (every
 // lane writes, lanes past the resource write zeros)
 __device__ __forceinline__ void lds_load4(const i32x4_t& srd, void* lds, uint32_t voff) {
@@ -354,8 +370,6 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
     rB2 = DUAL ? make_srd(B2p + kb * p.ldb + n0, rows * p.ldb * TS) : rB;
   }
 
-  auto stage_a = [&](int s) -> unsigned char* { return smem + s * C::STAGE; };
-  auto stage_b = [&](int s) -> unsigned char* { return smem + s * C::STAGE + C::A_BYTES; };
 
   // ---- row-indexed K (Mode::ExpertIdx: A; ExpertIdxB: B).  A wave's loads
   // of that operand's K-tile cover KW consecutive K-rows.  Each wave keeps
@@ -388,6 +402,51 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
     lds_load4(rI, smem + kidx_offset<C>() + (wave * NS + s) * 256, off);
   };
 
+  // ---- per-lane parts of the load offsets (bytes; 32-bit, every resource
+  // spans less than 2^31 bytes), computed once: issue() adds the K-tile's
+  // wave-uniform part, so a K-step's loads cost one add each.  An offset of
+  // kOob (rows past the segment end, B columns past N) stays past every
+  // resource after the add.  The LDS destinations are 32-bit LDS addresses.
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_void_p)smem));
+  uint32_t aoff[C::A_PW], boff_l[C::B_PW];
+  const uint32_t a_rowb = (uint32_t)(p.lda * TS), b_rowb = (uint32_t)(p.ldb * TS);  // row pitches
+#pragma unroll
+  for (int u = 0; u < C::A_PW; ++u) {
+    const int ins = wave * C::A_PW + u;
+    if constexpr (A_K) {
+      const int row = ins * RPIK + lane / CK;
+      const int c = (lane % CK) ^ kswz<CK>(row);
+      aoff[u] = arow[u] == kOob ? kOob : arow[u] + (uint32_t)(c * 8 * TS);
+    } else if constexpr (!KIDX_A) {
+      constexpr int RPI = 64 / RCA;
+      const int k = ins * RPI + lane / RCA;
+      const int c = (lane % RCA) ^ trswz<RCA>(k);
+      aoff[u] = (uint32_t)k * a_rowb + (uint32_t)(c * 8 * TS);
+    } else {
+      aoff[u] = 0;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < C::B_PW; ++u) {
+    const int ins = wave * C::B_PW + u;
+    if constexpr (B_K) {
+      const int row = ins * RPIK + lane / CK;
+      const int c = (lane % CK) ^ kswz<CK>(row);
+      boff_l[u] = (uint32_t)row * b_rowb + (uint32_t)(c * 8 * TS);
+    } else if constexpr (!KIDX_B) {
+      constexpr int PER_G = BK * RCB / 64;
+      constexpr int RPI = 64 / RCB;
+      const int gi = ins % PER_G;
+      const int k = gi * RPI + lane / RCB;
+      const int c = (lane % RCB) ^ trswz<RCB>(k);
+      bool ok = true;
+      if constexpr (MODE == Mode::Dense) ok = n0 + c * 8 < p.N;
+      boff_l[u] = ok ? (uint32_t)k * b_rowb + (uint32_t)(c * 8 * TS) : kOob;
+    } else {
+      boff_l[u] = 0;
+    }
+  }
+
   // ---- issue the loads of K-tile kt into LDS stage s (an indexed product
   // then loads the k_rows entries of tile kn into the stage's slot)
   auto issue = [&](int kt, int s, int kn) __attribute__((always_inline)) {
@@ -402,63 +461,56 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
 #pragma unroll
     for (int u = 0; u < C::A_PW; ++u) {
       const int ins = wave * C::A_PW + u;
-      unsigned char* dst = stage_a(s) + ins * 1024;
+      const uint32_t dst = lds0 + (uint32_t)(s * C::STAGE + ins * 1024);
       if constexpr (A_K) {
-        const int row = ins * RPIK + lane / CK;
-        const int c = (lane % CK) ^ kswz<CK>(row);
-        const uint32_t off = arow[u] == kOob ? kOob : arow[u] + (uint32_t)((kk + c * 8) * TS);
-        lds_load16(second ? rA2 : rA, dst, off);
+        lds_load16_at(second ? rA2 : rA, dst, aoff[u] + (uint32_t)kk * (uint32_t)TS);
       } else {
         constexpr int RPI = 64 / RCA;
         const int k = ins * RPI + lane / RCA;
-        const int c = (lane % RCA) ^ trswz<RCA>(k);
         const int kr = k0 + k;
         uint32_t off;
         if constexpr (KIDX_A) {
           // row k of the tile is entry u * RPI + lane / RCA of this wave's slot
+          const int c = (lane % RCA) ^ trswz<RCA>(k);
           const uint32_t n = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
               (uintptr_t)(ibase + (uint32_t)(s * 256 + u * RPI * 4)));
           const uint32_t ro = src_offset(n);
           off = (kr < k_len && ro != kOob) ? ro + (uint32_t)(c * 8 * TS) : kOob;
         } else {
-          off = kr < k_len ? (uint32_t)((kr * p.lda + c * 8) * TS) : kOob;
+          off = kr < k_len ? aoff[u] + (uint32_t)k0 * a_rowb : kOob;
         }
-        lds_load16(rA, dst, off);
+        lds_load16_at(rA, dst, off);
       }
     }
     // B
 #pragma unroll
     for (int u = 0; u < C::B_PW; ++u) {
       const int ins = wave * C::B_PW + u;
-      unsigned char* dst = stage_b(s) + ins * 1024;
+      const uint32_t dst = lds0 + (uint32_t)(s * C::STAGE + C::A_BYTES + ins * 1024);
       if constexpr (B_K) {
-        const int row = ins * RPIK + lane / CK;
-        const int c = (lane % CK) ^ kswz<CK>(row);
-        lds_load16(second ? rB2 : rB, dst, (uint32_t)((row * p.ldb + kk + c * 8) * TS));
+        lds_load16_at(second ? rB2 : rB, dst, boff_l[u] + (uint32_t)kk * (uint32_t)TS);
       } else {
         // group g holds instructions [g * PER_G, (g + 1) * PER_G): wave-uniform
         constexpr int PER_G = BK * RCB / 64;
         constexpr int RPI = 64 / RCB;
         const int g = ins / PER_G;
-        const int gi = ins - g * PER_G;
-        const int k = gi * RPI + lane / RCB;
-        const int c = (lane % RCB) ^ trswz<RCB>(k);
-        const int kr = k0 + k;
-        bool ok = true;
-        if constexpr (EXPERT) ok = kr < k_len;
-        if constexpr (MODE == Mode::Dense) ok = n0 + c * 8 < p.N;
         uint32_t off;
         if constexpr (KIDX_B) {
           // row k of the tile is entry u * RPI + lane / RCB of this wave's
           // slot (one group: ins = wave * B_PW + u)
+          const int k = (ins - g * PER_G) * RPI + lane / RCB;
+          const int c = (lane % RCB) ^ trswz<RCB>(k);
           const uint32_t n = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
               (uintptr_t)(ibase + (uint32_t)(s * 256 + u * RPI * 4)));
           const uint32_t ro = src_offset(n);
-          off = (ok && ro != kOob) ? ro + (uint32_t)(c * 8 * TS) : kOob;
+          off = (k0 + k < k_len && ro != kOob) ? ro + (uint32_t)(c * 8 * TS) : kOob;
+        } else if constexpr (EXPERT) {
+          const int k = (ins - g * PER_G) * RPI + lane / RCB;
+          off = k0 + k < k_len ? boff_l[u] + (uint32_t)k0 * b_rowb : kOob;
         } else {
-          off = ok ? (uint32_t)((kr * p.ldb + c * 8) * TS) : kOob;
+          off = boff_l[u] + (uint32_t)k0 * b_rowb;
         }
-        lds_load16((DUAL && g) ? rB2 : rB, dst, off);
+        lds_load16_at((DUAL && g) ? rB2 : rB, dst, off);
       }
     }
     if constexpr (KIDX) load_idx(kn, s);
