@@ -460,8 +460,7 @@ hipError_t bwd_stage(const BwdCall& c, int stage, int i, int* launches) {
       x.offpad = c.offpad;
       x.E = P.E;
       x.ldk = ldk;
-      if (launch_digitize(x, st) != hipSuccess) return hipErrorLaunchFailure;
-      *launches += 2;
+      if (launch_digitize(x, st, launches) != hipSuccess) return hipErrorLaunchFailure;
       run(launch_exact_wgrad(c.plane[8], c.plane[9], c.plane[2], c.plane[3], ldk, rg.offsets,
                              c.offpad, lo_d, c.acc_hi[2], P.E, P.F, P.H, init, st));
     } else {

@@ -439,9 +439,10 @@ hipError_t launch_colmax_rows(const void* a, const void* u, const void* h, const
   return hipGetLastError();
 }
 
-hipError_t launch_digitize(const ExactChunk& x, hipStream_t st) {
+hipError_t launch_digitize(const ExactChunk& x, hipStream_t st, int* launches) {
   pad_offsets_kernel<<<1, 1024, 0, st>>>(x.offsets, x.E, x.offpad);
   if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
+  if (launches) ++*launches;
   DigitArgs a{};
   const DigitPlanesSrc* in[kDigitMats] = {&x.X, &x.dY, &x.da, &x.du, &x.hg};
   int cmax_cols = 0;
@@ -457,7 +458,9 @@ hipError_t launch_digitize(const ExactChunk& x, hipStream_t st) {
   a.ldk = x.ldk;
   const dim3 grid((unsigned)(x.ldk / 64), (unsigned)ceil_div(cmax_cols, 64), kDigitMats);
   digitize_kernel<<<grid, kThreads, 0, st>>>(a);
-  return hipGetLastError();
+  if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
+  if (launches) ++*launches;
+  return hipSuccess;
 }
 
 hipError_t launch_exact_wgrad(const int8_t* a_hi, const int8_t* a_lo, const int8_t* b_hi,

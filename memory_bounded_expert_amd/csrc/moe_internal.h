@@ -182,8 +182,9 @@ struct ExactChunk {
   int E;
   int64_t ldk;
 };
-// The chunk's padded segment starts, then the digit planes of all five.
-hipError_t launch_digitize(const ExactChunk& x, hipStream_t st);
+// The chunk's padded segment starts, then the digit planes of all five
+// (two kernels, added to *launches).
+hipError_t launch_digitize(const ExactChunk& x, hipStream_t st, int* launches);
 // acc64[e][m][n] (init: =, else +=) sum over expert e's chunk rows of
 // vA[m][k] vB[n][k], from digit planes; the 64-bit accumulator is split into
 // c_lo (low words) and c_hi.  M % 128 == 0, N % 64 == 0.
