@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void dwr_kernel(const T* __restrict__ X,
   constexpr int CPB = COLS / EPC;
   static_assert(COLS % EPC == 0 && kThreads % CPB == 0 && COLS <= kThreads, "column block");
   constexpr int RG = kThreads / CPB;
-  constexpr int UNR = 4;
+  constexpr int UNR = 16;
   __shared__ float part[RG][COLS + 1];
   __shared__ int64_t tok[kThreads];
   __shared__ float dl[kThreads];
