@@ -759,8 +759,9 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
     // C += tile (fp32 read-modify-write), or C = tile with acc_init or
     // acc_chain (the accumulators then already hold the whole sum).  Each
     // wave moves its own block through its LDS share (AccGeom); the old
-    // values of slice s+1 are requested before slice s is added and stored,
-    // so the read latency overlaps the previous slice's work.  Each element
+    // values of slices s+1 .. s+PD are in flight while slice s is added and
+    // stored (the fragment registers are free by then), so the reads'
+    // latency overlaps PD slices' work.  Each element
     // is old + new in one fp32 add.  The operand stages are free once every
     // wave's last fragment reads are done (the barrier); after it each wave
     // touches only its own share.  Rows past row_end are neither read nor
@@ -781,11 +782,14 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
       return reinterpret_cast<f32x4_t*>(Cg + (int64_t)grow(s, u) * p.ldc + cw0 + c4 * 4);
     };
     const bool accumulate = !p.acc_init && !p.acc_chain;
-    f32x4_t old[2][AG::PER];
+    constexpr int PD = 3;  // slices of old values requested ahead
+    f32x4_t old[PD + 1][AG::PER];
     if (accumulate) {
 #pragma unroll
-      for (int u = 0; u < AG::PER; ++u)
-        if (grow(0, u) < row_end) old[0][u] = __builtin_nontemporal_load(gptr(0, u));
+      for (int s0 = 0; s0 < PD && s0 < AG::NSUB; ++s0)
+#pragma unroll
+        for (int u = 0; u < AG::PER; ++u)
+          if (grow(s0, u) < row_end) old[s0][u] = __builtin_nontemporal_load(gptr(s0, u));
     }
     lds_barrier();  // every wave's last fragment reads are done
 #pragma unroll
@@ -799,16 +803,16 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
           for (int q = 0; q < 4; ++q)
             stg[(i * 16 + 4 * lg + q) * AG::LD + j * 16 + l16] = acc[g][sl * AG::FS + i][j][q];
       wave_lds_sync();
-      if (accumulate && s + 1 < AG::NSUB) {
+      if (accumulate && s + PD < AG::NSUB) {
 #pragma unroll
         for (int u = 0; u < AG::PER; ++u)
-          if (grow(s + 1, u) < row_end) old[(s + 1) & 1][u] = __builtin_nontemporal_load(gptr(s + 1, u));
+          if (grow(s + PD, u) < row_end) old[(s + PD) % (PD + 1)][u] = __builtin_nontemporal_load(gptr(s + PD, u));
       }
 #pragma unroll
       for (int u = 0; u < AG::PER; ++u) {
         const int idx = lane + u * 64, r = idx / AG::VW, c4 = idx - r * AG::VW;
         const f32x4_t add = *reinterpret_cast<const f32x4_t*>(stg + r * AG::LD + c4 * 4);
-        if (grow(s, u) < row_end) __builtin_nontemporal_store(accumulate ? old[s & 1][u] + add : add, gptr(s, u));
+        if (grow(s, u) < row_end) __builtin_nontemporal_store(accumulate ? old[s % (PD + 1)][u] + add : add, gptr(s, u));
       }
       wave_lds_sync();  // this slice's reads are done before the next slice's writes
     }
