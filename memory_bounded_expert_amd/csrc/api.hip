@@ -247,13 +247,15 @@ int forward_impl(const moe_plan_t& P, const void* X, const void* W_r, const floa
   for (int i = 0; i < P.K; ++i) {
     const ChunkGeom g = chunk_geom(P.N, P.K, P.k, i);
     const int64_t R = (int64_t)P.k * g.n;
-    const RowsGeom rg = rows_geom(pb, P, i, R);
+    RowsGeom rg = rows_geom(pb, P, i, R);
+    rg.kt_rows = h_kt_rows(P);
     const int32_t* perm_i = pb.perm + g.pair_base;
     // a split plan runs the gate/up product over its two split lists (the
     // short segments' 128-row tiles and the rest) as one launch
     const bool split = pb.small_tiles != nullptr;
-    const RowsGeom rgl = split ? long_geom(pb, P, i, R) : rg;
-    const RowsGeom rgs = split ? small_geom(pb, P, i, R) : rg;
+    RowsGeom rgl = split ? long_geom(pb, P, i, R) : rg;
+    RowsGeom rgs = split ? small_geom(pb, P, i, R) : rg;
+    rgl.kt_rows = rgs.kt_rows = rg.kt_rows;
     const RowsGeom* gs = split ? &rgs : nullptr;
     if (fused) {
       MOE_CHECK(gemm_up_swiglu(P.dtype, rgl, X, W_gate, W_up, h, nullptr, nullptr, P.H, P.F, st,
@@ -677,14 +679,16 @@ MOE_API int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk
   } else {
     const ChunkGeom g = chunk_geom(P.N, P.K, P.k, chunk);
     const int64_t R = (int64_t)P.k * g.n;
-    const RowsGeom rg = rows_geom(pb, P, chunk, R);
+    RowsGeom rg = rows_geom(pb, P, chunk, R);
+    rg.kt_rows = h_kt_rows(P);
     const int32_t* perm_i = pb.perm + g.pair_base;
     void* xp = ws + L.xp;
     void* o = ws + L.o;
     void* h = ws + L.h;
     const bool split = pb.small_tiles != nullptr;  // the lists the forward call uses
-    const RowsGeom rgl = split ? long_geom(pb, P, chunk, R) : rg;
-    const RowsGeom rgs = split ? small_geom(pb, P, chunk, R) : rg;
+    RowsGeom rgl = split ? long_geom(pb, P, chunk, R) : rg;
+    RowsGeom rgs = split ? small_geom(pb, P, chunk, R) : rg;
+    rgl.kt_rows = rgs.kt_rows = rg.kt_rows;
     const RowsGeom* gs = split ? &rgs : nullptr;
     switch (stage) {
       case MOE_STAGE_GATHER:

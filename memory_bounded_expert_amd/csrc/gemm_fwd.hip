@@ -84,6 +84,11 @@ hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const vo
   p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
   const bool save = a != nullptr;
   const bool big = g.row_tile == kRowTileLarge;
+  if (g.kt_rows > 0) {
+    // the forward's K-tile-major h (written here, read by the down projection)
+    if (dtype != MOE_BF16 || save || !big || F % 32) return hipErrorInvalidValue;
+    p.c_kt = g.kt_rows * 32;
+  }
   const int bn = (dtype == MOE_BF16 && !save && !big && F % 256 == 0) ? 256 : (F % 128 == 0 ? 128 : 64);
   p.ntiles = F / bn;
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
@@ -110,6 +115,11 @@ hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd
   p.row_scale = row_gates;
   p.N = H; p.K = F;
   p.tiles = g.tiles; p.tile_count = g.tile_count; p.offsets = g.offsets;
+  if (g.kt_rows > 0) {
+    // h K-tile-major: read by the 256-row shapes, whose K-tiles are 32 wide
+    if (dtype != MOE_BF16 || g.row_tile != kRowTileLarge || F % 32) return hipErrorInvalidValue;
+    p.a_kt = g.kt_rows * 32;
+  }
   const int bn = g.row_tile == kRowTileLarge ? (H % 256 == 0 ? 256 : 128)
                  : (dtype == MOE_BF16 && H % 512 == 0) ? 512 : pick_bn(H, true);
   p.ntiles = H / bn;

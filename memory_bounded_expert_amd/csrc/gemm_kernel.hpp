@@ -61,6 +61,8 @@ struct Params {
   const void* B2;  // second operand group (DUAL) or second K segment (KCAT)
   int64_t ldb;
   int64_t b_estride;  // elements between experts' B (Rows mode)
+  int64_t a_kt;  // > 0: A K-tile-major, element (r, k) at (k / 32) a_kt + 32 r + k % 32
+  int64_t c_kt;  // > 0: C likewise, element (r, n) at (n / 32) c_kt + 32 r + n % 32
   void* C;
   void* C2;
   void* C3;

@@ -336,6 +336,16 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
           if ((uint64_t)src < (uint64_t)p.a_src_rows) arow[u] = (uint32_t)((int64_t)src * p.lda * TS);
         }
       }
+    } else if (p.a_kt) {
+      // K-tile-major A (BK = 32: one block per K-tile): the tile's rows of a
+      // block are 64-byte rows; rows past the tile are masked (the resource
+      // runs on through the other rows and blocks)
+      rA = make_srd(Ap + (int64_t)m0 * 32, ((int64_t)p.K / 32 * p.a_kt - (int64_t)m0 * 32) * TS);
+#pragma unroll
+      for (int u = 0; u < C::A_PW; ++u) {
+        const int row = (wave * C::A_PW + u) * RPIK + lane / CK;
+        arow[u] = row < rows ? (uint32_t)(row * 32 * TS) : kOob;
+      }
     } else {
       rA = make_srd(Ap + (int64_t)m0 * p.lda, rows * p.lda * TS);
 #pragma unroll
@@ -410,6 +420,8 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_void_p)smem));
   uint32_t aoff[C::A_PW], boff_l[C::B_PW];
   const uint32_t a_rowb = (uint32_t)(p.lda * TS), b_rowb = (uint32_t)(p.ldb * TS);  // row pitches
+  // bytes from one 32-wide K block of a K-contiguous A to the next
+  const uint32_t a_ktb = p.a_kt ? (uint32_t)(p.a_kt * TS) : (uint32_t)(32 * TS);
 #pragma unroll
   for (int u = 0; u < C::A_PW; ++u) {
     const int ins = wave * C::A_PW + u;
@@ -463,7 +475,7 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
       const int ins = wave * C::A_PW + u;
       const uint32_t dst = lds0 + (uint32_t)(s * C::STAGE + ins * 1024);
       if constexpr (A_K) {
-        lds_load16_at(second ? rA2 : rA, dst, aoff[u] + (uint32_t)kk * (uint32_t)TS);
+        lds_load16_at(second ? rA2 : rA, dst, aoff[u] + (uint32_t)(kk >> 5) * a_ktb);
       } else {
         constexpr int RPI = 64 / RCA;
         const int k = ins * RPI + lane / RCA;
@@ -1021,8 +1033,10 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
         for (int idx = tid; idx < SR * V; idx += C::THREADS) {
           const int r = idx / V, c = idx - r * V;
           if (row0 + r >= row_end) break;  // rows ascend with idx
-          *reinterpret_cast<u32x4_t*>(Cbase + (int64_t)(row0 + r) * p.ldc + n0 + c * VE) =
-              *reinterpret_cast<const u32x4_t*>(stg + r * LD + c * VE);
+          const int col = n0 + c * VE;
+          OT* dst = p.c_kt ? Cbase + (int64_t)(col >> 5) * p.c_kt + (int64_t)(row0 + r) * 32 + (col & 31)
+                           : Cbase + (int64_t)(row0 + r) * p.ldc + col;
+          *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(stg + r * LD + c * VE);
         }
       }
     };

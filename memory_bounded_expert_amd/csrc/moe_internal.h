@@ -279,7 +279,16 @@ struct RowsGeom {
   const int32_t* offsets;
   int64_t grid_m;  // upper bound on the chunk's M-tiles
   int row_tile;    // rows per M-tile (kRowTile or kRowTileLarge)
+  // > 0: the forward's h is stored K-tile-major -- 32-column blocks, each
+  // holding all kt_rows rows of those 32 columns (64 bytes per row) -- so
+  // that the down projection's A loads read whole 16 KiB blocks
+  int64_t kt_rows = 0;
 };
+// The rows of the forward's K-tile-major h (bf16 chunks on 256-row tiles,
+// whose gate/up epilogue and down projection take it so), else 0.
+inline int64_t h_kt_rows(const moe_plan_t& p) {
+  return (p.dtype == MOE_BF16 && row_tile_for(p) == kRowTileLarge) ? (int64_t)p.k * p.c_eff : 0;
+}
 // h = silu(Xp W_gate[e]) * (Xp W_up[e]) per expert segment; save_au also
 // stores a and u.  With rows != nullptr (bf16 only), Xp is not a buffer:
 // row r is row rows[r] / k of X (x_rows rows), read straight from X.
