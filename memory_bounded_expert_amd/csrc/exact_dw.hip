@@ -352,6 +352,8 @@ __global__ __launch_bounds__(kThreads, 2) void exact_wgrad_kernel(const ExactPar
   // of a write land in distinct banks), then added into the 64-bit
   // accumulator four columns at a time: 16-byte, row-contiguous accesses to
   // the low and high words, all of a lane's old values requested first
+  // (non-temporal: each accumulator word is read and written once per
+  // launch, and the digit planes that other tiles read stay in L2)
   constexpr int kLd = 36;
   gemm::lds_barrier();  // every wave is done with the operand stages
   int64_t* stg = reinterpret_cast<int64_t*>(smem + wave * (64 * kLd * 8));
@@ -373,8 +375,8 @@ __global__ __launch_bounds__(kThreads, 2) void exact_wgrad_kernel(const ExactPar
     const int item = lane + 64 * it, r = item >> 3, c4 = (item & 7) * 4;
     base[it] = ((int64_t)e * p.M + m0 + wm * 64 + r) * p.N + n0 + wn * 32 + c4;
     if (!p.init) {
-      olo[it] = *reinterpret_cast<const u32x4_t*>(p.c_lo + base[it]);
-      ohi[it] = *reinterpret_cast<const u32x4_t*>(p.c_hi + base[it]);
+      olo[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.c_lo + base[it]));
+      ohi[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.c_hi + base[it]));
     }
   }
 #pragma unroll
@@ -388,8 +390,8 @@ __global__ __launch_bounds__(kThreads, 2) void exact_wgrad_kernel(const ExactPar
       lo[c] = (uint32_t)(uint64_t)v;
       hi[c] = (uint32_t)(uint64_t)(v >> 32);
     }
-    *reinterpret_cast<u32x4_t*>(p.c_lo + base[it]) = lo;
-    *reinterpret_cast<u32x4_t*>(p.c_hi + base[it]) = hi;
+    __builtin_nontemporal_store(lo, reinterpret_cast<u32x4_t*>(p.c_lo + base[it]));
+    __builtin_nontemporal_store(hi, reinterpret_cast<u32x4_t*>(p.c_hi + base[it]));
   }
 }
 
