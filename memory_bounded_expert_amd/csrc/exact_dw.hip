@@ -179,14 +179,15 @@ struct DigitArgs {
   int64_t ldk;
 };
 
+constexpr int kDigitColBlocks = 4;  // 64-column blocks per work-group
 __global__ __launch_bounds__(kThreads) void digitize_kernel(const DigitArgs a) {
   __shared__ int8_t shi[64][64 + 16];
   __shared__ int8_t slo[64][64 + 16];
   __shared__ int se;
   const DigitSrc& s = a.s[blockIdx.z];
-  const int c0 = blockIdx.y * 64;
   const int rp0 = blockIdx.x * 64;
-  if (c0 >= s.C || rp0 >= a.offpad[a.E]) return;  // (uniform over the work-group)
+  const int cb0 = blockIdx.y * kDigitColBlocks * 64;
+  if (cb0 >= s.C || rp0 >= a.offpad[a.E]) return;  // (uniform over the work-group)
   const int t = threadIdx.x;
   if (t == 0) {
     // the expert whose padded segment holds rp0: the last e with offpad[e] <= rp0
@@ -202,34 +203,52 @@ __global__ __launch_bounds__(kThreads) void digitize_kernel(const DigitArgs a) {
   const int rel0 = rp0 - a.offpad[e];
   const int cnt = a.offsets[e + 1] - a.offsets[e];
   const int rbase = a.offsets[e];
-  const int cc = t & 7;  // this thread's 8 columns: c0 + cc*8 .. +8
-  int ex[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    ex[j] = col_exp(s.cmax[(s.per_expert ? (int64_t)e * s.C : 0) + c0 + cc * 8 + j]);
+  const int cc = t & 7;  // this thread's 8 columns of a block: c0 + cc*8 .. +8
+  // this thread's two source rows (64-row block, two passes of 32), the same
+  // for every column block
+  int64_t srow[2];
+  bool have[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int r = (t + q * kThreads) >> 3;  // 0..63
     const int rel = rel0 + r;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (rel < cnt) {
-      const int row = rbase + rel;
-      const int64_t sr = s.rows ? (int64_t)(s.rows[row] / s.row_div) : (int64_t)row;
-      unpack16(*reinterpret_cast<const u32x4_t*>(s.src + sr * s.ld + c0 + cc * 8), v, bf16_t());
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int dh, dl;
-      to_digits(v[j], ex[j], dh, dl);
-      shi[cc * 8 + j][r] = (int8_t)dh;
-      slo[cc * 8 + j][r] = (int8_t)dl;
-    }
+    have[q] = rel < cnt;
+    const int row = rbase + (have[q] ? rel : 0);
+    srow[q] = s.rows ? (int64_t)(s.rows[row] / s.row_div) : (int64_t)row;
   }
-  __syncthreads();
-  const int c = t >> 2, part = t & 3;
-  const int64_t o = (int64_t)(c0 + c) * a.ldk + rp0 + part * 16;
-  *reinterpret_cast<u32x4_t*>(s.hi + o) = *reinterpret_cast<const u32x4_t*>(&shi[c][part * 16]);
-  *reinterpret_cast<u32x4_t*>(s.lo + o) = *reinterpret_cast<const u32x4_t*>(&slo[c][part * 16]);
+  for (int b = 0; b < kDigitColBlocks; ++b) {
+    const int c0 = cb0 + b * 64;
+    if (c0 >= s.C) break;  // (uniform)
+    // both rows' loads first, then their digits
+    u32x4_t raw[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      raw[q] = have[q] ? *reinterpret_cast<const u32x4_t*>(s.src + srow[q] * s.ld + c0 + cc * 8)
+                       : u32x4_t{0u, 0u, 0u, 0u};
+    int ex[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ex[j] = col_exp(s.cmax[(s.per_expert ? (int64_t)e * s.C : 0) + c0 + cc * 8 + j]);
+    if (b > 0) __syncthreads();  // the previous block's planes have left LDS
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = (t + q * kThreads) >> 3;
+      float v[8];
+      unpack16(raw[q], v, bf16_t());
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        int dh, dl;
+        to_digits(v[j], ex[j], dh, dl);
+        shi[cc * 8 + j][r] = (int8_t)dh;
+        slo[cc * 8 + j][r] = (int8_t)dl;
+      }
+    }
+    __syncthreads();
+    const int c = t >> 2, part = t & 3;
+    const int64_t o = (int64_t)(c0 + c) * a.ldk + rp0 + part * 16;
+    *reinterpret_cast<u32x4_t*>(s.hi + o) = *reinterpret_cast<const u32x4_t*>(&shi[c][part * 16]);
+    *reinterpret_cast<u32x4_t*>(s.lo + o) = *reinterpret_cast<const u32x4_t*>(&slo[c][part * 16]);
+  }
 }
 
 // ---- the exact weight-gradient product: acc64[e][m][n] (+)= sum over the
@@ -458,7 +477,8 @@ hipError_t launch_digitize(const ExactChunk& x, hipStream_t st, int* launches) {
   a.offpad = x.offpad;
   a.E = x.E;
   a.ldk = x.ldk;
-  const dim3 grid((unsigned)(x.ldk / 64), (unsigned)ceil_div(cmax_cols, 64), kDigitMats);
+  const dim3 grid((unsigned)(x.ldk / 64), (unsigned)ceil_div(cmax_cols, 64 * kDigitColBlocks),
+                  kDigitMats);
   digitize_kernel<<<grid, kThreads, 0, st>>>(a);
   if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
   if (launches) ++*launches;
