@@ -119,6 +119,14 @@ RowsGeom rows_geom(const PlanBuffers& b, const moe_plan_t& P, int i, int64_t R) 
   return g;
 }
 
+// Whether a split plan's down projection runs over its two lists: only
+// where experts average fewer than two 256-row tiles per chunk (with more,
+// segments of at most 128 rows are rare, and the two-list launch measured
+// about 2% slower than the one-list kernel on the same tiles).
+bool split_down(bool split, int64_t R, const moe_plan_t& P) {
+  return split && R < 2 * (int64_t)kRowTileLarge * P.E;
+}
+
 // The long segments' list of a split plan (row_tile-row tiles).
 RowsGeom long_geom(const PlanBuffers& b, const moe_plan_t& P, int i, int64_t R) {
   RowsGeom g = rows_geom(b, P, i, R);
@@ -267,7 +275,8 @@ int forward_impl(const moe_plan_t& P, const void* X, const void* W_r, const floa
     }
     // the gates scale the expert rows in the down projection's epilogue; the
     // combine then sums each token's k rows
-    MOE_CHECK(gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st, pb.row_gates + g.pair_base));
+    MOE_CHECK(gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st, pb.row_gates + g.pair_base,
+                        split_down(split, R, P) ? &rgl : nullptr, gs));
     MOE_CHECK(launch_combine(P.dtype, o, pb.pos, Y, P.N, P.K, i, g.n, P.k, P.H, st));
   }
   fill_stats(stats, P, launches, L.total,
@@ -701,7 +710,8 @@ MOE_API int moe_debug_stage(const moe_plan_t* plan, int32_t stage, int32_t chunk
                                      P.F, st, nullptr, 1, 0, gs);
         break;
       case MOE_STAGE_GEMM_DOWN:
-        err = gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st, pb.row_gates + g.pair_base);
+        err = gemm_down(P.dtype, rg, h, W_down, o, P.H, P.F, st, pb.row_gates + g.pair_base,
+                        split_down(split, R, P) ? &rgl : nullptr, gs);
         break;
       default:
         err = launch_combine(P.dtype, o, pb.pos, Y, P.N, P.K, chunk, g.n, P.k, P.H, st);

@@ -106,7 +106,8 @@ hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const vo
 }
 
 hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd, void* O, int H,
-                     int F, hipStream_t st, const float* row_gates) {
+                     int F, hipStream_t st, const float* row_gates, const RowsGeom* gl,
+                     const RowsGeom* gs) {
   if (g.grid_m == 0) return hipSuccess;
   Params p{};
   p.A = h; p.lda = F;
@@ -123,6 +124,23 @@ hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd
   const int bn = g.row_tile == kRowTileLarge ? (H % 256 == 0 ? 256 : 128)
                  : (dtype == MOE_BF16 && H % 512 == 0) ? 512 : pick_bn(H, true);
   p.ntiles = H / bn;
+  if (gl && gs && dtype == MOE_BF16 && g.row_tile == kRowTileLarge && H % 512 == 0) {
+    // the long segments' 256-row tiles and the short ones' 128 x 512 tiles
+    // (K-tiles 32 wide, as the K-tile-major h needs) in one launch
+    // (128 rows: twice the weight bytes in flight per stage for a segment
+    // of few rows).  Below four rounds of work-groups the larger tiles cost
+    // more in the launch's tail than that gains, and the launch runs g's
+    // unsplit list in 256-row tiles instead.
+    Params pl = p, ps = p;
+    pl.tiles = gl->tiles; pl.tile_count = gl->tile_count;
+    ps.tiles = gs->tiles; ps.tile_count = gs->tile_count;
+    ps.ntiles = H / 512;
+    // the first grid also covers g's (the unsplit list's ids start at 0)
+    return launch_lds_pair<RowsGemm<Big<256>, false, true, false, false, Epi::Store>,
+                           RowsGemm<Shape<128, 512, 2, 4, 32, 1>, false, true, false, false, Epi::Store>,
+                           true>(pl, (int)(std::max(gl->grid_m, g.grid_m) * pl.ntiles), ps,
+                                 (int)(gs->grid_m * ps.ntiles), st, &p, 4 * kCus);
+  }
   const dim3 grid((unsigned)(g.grid_m * p.ntiles));
   return dtype == MOE_BF16 ? down_bf16(p, grid, bn, g.row_tile, st) : down_t<float>(p, grid, bn, st);
 }

@@ -189,6 +189,8 @@ __device__ __forceinline__ void transpose_block(const u32x4_t* in, u32x4_t* out,
 // with its own L2.  Renumbers id L of a grid of `total` work-groups so that
 // every XCD runs one contiguous range of the new ids (a bijection on
 // [0, total)).
+constexpr int kCus = 256;  // compute units (MI355X: 8 XCDs of 32)
+
 __device__ __forceinline__ int xcd_contiguous(int L, int total) {
   const int xcd = L & 7, slot = L >> 3;
   const int q = total >> 3, r = total & 7;

@@ -238,7 +238,7 @@ constexpr int lds_bytes() {
 }
 
 // The work-group's whole product.  bid is the work-group's index in a Rows
-// grid (a pair launch offsets the second product's ids); the other modes
+// grid (in a pair launch, its index in its own list's grid); the other modes
 // read blockIdx themselves.
 template <Mode MODE, class S, bool DUAL, bool A_K, bool B_K, bool KCAT, Epi EPI>
 __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
@@ -1148,38 +1148,48 @@ struct RowsGemm {
 // running them side by side overlaps the two rather than taking them one
 // after the other; the shorter 128-row tiles last keep the launch's tail
 // short (interleaving to the end measured 6% slower on balanced routing).
-template <class G1, class G2>
+// With ALT, a launch whose two lists come to fewer than split_min
+// work-groups runs G1 over pu instead (the chunk's unsplit tile list, as a
+// single-product launch would), where G2's larger tiles would leave too few
+// rounds.
+template <class G1, class G2, bool ALT = false>
 __global__ __launch_bounds__(64 * G1::C::WAVES)
 __attribute__((amdgpu_waves_per_eu(G1::S::WG_PER_CU * G1::C::WAVES / 4))) void gemm_lds_pair_kernel(
-    const Params p1, const Params p2) {
+    const Params p1, const Params p2, const Params pu, int split_min) {
   static_assert(G1::C::WAVES == G2::C::WAVES && G1::S::WG_PER_CU == G2::S::WG_PER_CU,
                 "paired products need the same work-group shape");
   const int b = (int)blockIdx.x;
   const int t1 = __builtin_amdgcn_readfirstlane(*p1.tile_count * p1.ntiles);
   const int t2 = __builtin_amdgcn_readfirstlane(*p2.tile_count * p2.ntiles);
-  // ids with b % 8 == x reach XCD x in the order j = b / 8; that XCD holds
-  // c1 ids of the first list (those L < t1 with L % 8 == x) and c2 of the second
-  const int x = b & 7, j = b >> 3;
-  const int c1 = t1 > x ? (t1 - x + 7) >> 3 : 0;
-  const int c2 = t2 > x ? (t2 - x + 7) >> 3 : 0;
-  if (j >= c1 + c2) return;
-  // the XCD's last round (one work-group per CU, 32 CUs) takes second-list
-  // tiles only; before it, ci ids interleave all c1 first-list tiles with
-  // the other second-list ones
-  constexpr int kXcdCus = 32;
-  const int R = min(c2, kXcdCus);
-  const int ci = c1 + c2 - R;
-  if (j >= ci) {
-    G2::run(p2, x + 8 * (c2 - R + (j - ci)));
-    return;
+  bool whole = false;
+  if constexpr (ALT) whole = t1 + t2 < split_min;
+  int L = b;
+  bool first = whole;
+  if (!whole) {
+    // ids with b % 8 == x reach XCD x in the order j = b / 8; that XCD holds
+    // c1 ids of the first list (those L < t1 with L % 8 == x) and c2 of the second
+    const int x = b & 7, j = b >> 3;
+    const int c1 = t1 > x ? (t1 - x + 7) >> 3 : 0;
+    const int c2 = t2 > x ? (t2 - x + 7) >> 3 : 0;
+    if (j >= c1 + c2) return;
+    // the XCD's last round (one work-group per CU) takes second-list tiles
+    // only; before it, ci ids interleave all c1 first-list tiles with the
+    // other second-list ones
+    const int R = min(c2, kCus / 8);
+    const int ci = c1 + c2 - R;
+    L = x + 8 * (c2 - R + (j - ci));
+    if (j < ci) {
+      // first-list tiles among this XCD's first j ids: ceil(j c1 / ci)
+      const int j1 = (int)(((int64_t)j * c1 + ci - 1) / ci);
+      const int j1n = (int)(((int64_t)(j + 1) * c1 + ci - 1) / ci);
+      first = j1n > j1;
+      L = first ? x + 8 * j1 : x + 8 * (j - j1);
+    }
   }
-  // first-list tiles among this XCD's first j ids: ceil(j c1 / ci)
-  const int j1 = (int)(((int64_t)j * c1 + ci - 1) / ci);
-  const int j1n = (int)(((int64_t)(j + 1) * c1 + ci - 1) / ci);
-  if (j1n > j1)
-    G1::run(p1, x + 8 * j1);
+  if (first)
+    G1::run(ALT && whole ? pu : p1, L);
   else
-    G2::run(p2, x + 8 * (j - j1));
+    G2::run(p2, L);
 }
 
 template <class KERN>
@@ -1201,10 +1211,13 @@ hipError_t launch_lds(const Params& p, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-// G1 over a 1-D Rows grid of n1 work-groups and G2 over n2, as one kernel.
-template <class G1, class G2>
-hipError_t launch_lds_pair(const Params& p1, int n1, const Params& p2, int n2, hipStream_t st) {
-  auto kern = gemm_lds_pair_kernel<G1, G2>;
+// G1 over a 1-D Rows grid of n1 work-groups and G2 over n2, as one kernel
+// (with pu, as gemm_lds_pair_kernel's ALT: n1 must then cover pu's grid).
+template <class G1, class G2, bool ALT = false>
+hipError_t launch_lds_pair(const Params& p1, int n1, const Params& p2, int n2, hipStream_t st,
+                           const Params* pu = nullptr, int split_min = 0) {
+  if (ALT != (pu != nullptr)) return hipErrorInvalidValue;
+  auto kern = gemm_lds_pair_kernel<G1, G2, ALT>;
   constexpr int l1 = G1::C::NS * G1::C::STAGE, l2 = G2::C::NS * G2::C::STAGE;
   constexpr int lds = l1 > l2 ? l1 : l2;
   static bool attr_set = false;
@@ -1213,7 +1226,7 @@ hipError_t launch_lds_pair(const Params& p1, int n1, const Params& p2, int n2, h
   // then gets at least as many ids as its tiles of both lists (the kernel
   // reads the actual counts)
   const int n1p = (n1 + 7) & ~7;
-  kern<<<dim3((unsigned)(n1p + n2)), G1::C::THREADS, lds, st>>>(p1, p2);
+  kern<<<dim3((unsigned)(n1p + n2)), G1::C::THREADS, lds, st>>>(p1, p2, pu ? *pu : p1, split_min);
   return hipGetLastError();
 }
 

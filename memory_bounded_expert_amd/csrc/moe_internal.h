@@ -301,8 +301,12 @@ hipError_t gemm_up_swiglu(int dtype, const RowsGeom& g, const void* Xp, const vo
                           const RowsGeom* gs = nullptr);
 // O[r] = row_gates[r] (h[r] W_down[e]): each chunk row scaled by its pair's
 // gate before the one rounding (row_gates as the planner lays them out).
+// With gl and gs (a split plan's two lists; bf16, 256-row tiles, H a
+// multiple of 512), gl's 256-row tiles and gs's 128-row tiles run as one
+// launch; otherwise g's tiles.
 hipError_t gemm_down(int dtype, const RowsGeom& g, const void* h, const void* Wd, void* O, int H,
-                     int F, hipStream_t st, const float* row_gates);
+                     int F, hipStream_t st, const float* row_gates,
+                     const RowsGeom* gl = nullptr, const RowsGeom* gs = nullptr);
 // dh = dYp W_down[e]^T (fp32 out)
 hipError_t gemm_dh(int dtype, const RowsGeom& g, const void* dYp, const void* Wd, float* dh, int H,
                    int F, hipStream_t st);
