@@ -282,6 +282,48 @@ def test_split_tile_lists_bf16():
     run_workload(wl.name, full=False, wl=wl, reduced=(wl.N, wl.c))
 
 
+# The down projection of a split plan with H a multiple of 512, whose experts
+# average fewer than 512 rows per chunk, runs the short segments in 128 x 512
+# tiles beside the long ones' 256-row tiles in one launch when the two lists
+# come to 1,024 work-groups or more (the long list's M-tiles times H/256 plus
+# the short segments times H/512), and the unsplit 256-row list below that.
+# Zipf-routed, H = 4096, top-4 over 64 experts: K = 2 chunks of 3000 tokens
+# (F = 256) take the two lists, K = 2 chunks of 2000 tokens (F = 128) the
+# unsplit list; both unchunked comparison runs take the two lists.
+SPLIT_DOWN = datagen.WORKLOADS["zipf_bf16"].with_(
+    name="split_down_bf16", N=6000, H=4096, E=64, k=4, F=256, c=3000, K_max=16)
+SPLIT_DOWN_FEW = datagen.WORKLOADS["zipf_bf16"].with_(
+    name="split_down_few_bf16", N=4000, H=4096, E=64, k=4, F=128, c=2000, K_max=16)
+
+
+def _down_work_groups(wl, K):
+    """Per chunk, the split down launch's work-groups under the fp64 routing."""
+    inp = datagen.Inputs(wl, experts=False)
+    idx = oracle.topk_select(inp.to_f64(inp.X) @ inp.f64("Wr") + inp.bias, wl.k)
+    out = []
+    for i in range(K):
+        cnt = np.bincount(idx[i::K].reshape(-1), minlength=wl.E)
+        long_tiles = sum(-(-int(c) // 256) for c in cnt if c > 128)
+        short = int(np.count_nonzero((cnt > 0) & (cnt <= 128)))
+        assert long_tiles > 0 and short > 0
+        out.append(long_tiles * (wl.H // 256) + short * (wl.H // 512))
+    return out
+
+
+@pytest.mark.parametrize("wl,split", [(SPLIT_DOWN, True), (SPLIT_DOWN_FEW, False)],
+                         ids=["two_lists", "unsplit"])
+def test_split_down_projection_bf16(wl, split):
+    plan = plan_for(wl)
+    assert plan.K == 2 and wl.H % 512 == 0
+    assert 96 * wl.E <= wl.k * plan.c_eff < 512 * wl.E
+    wgs = _down_work_groups(wl, plan.K)
+    say(f"[{wl.name}] split down work-groups per chunk {wgs}")
+    # clear of the 1,024 threshold, so that routing flips within the fp32
+    # bound cannot move a chunk across it
+    assert all((w >= 1100) if split else (w <= 980) for w in wgs)
+    run_workload(wl.name, full=False, wl=wl, reduced=(wl.N, wl.c))
+
+
 # X of 2^31 bytes or more does not fit one buffer resource, so the bf16
 # forward gathers the permuted rows into their buffer (two H-wide buffers, the
 # whole bound) instead of reading them from X inside the GEMM, and the
