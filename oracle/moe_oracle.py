@@ -344,7 +344,7 @@ def backward_tokens(x_rows, dy_rows, idx_rows, gate_rows, experts: Callable[[int
 
 
 # ----------------------------------------------------------------------------
-# Rounding bound used to judge routing flips between fp32 and fp64 logits
+# Rounding bound that decides which routing flips between fp32 and fp64 logits are allowed
 # ----------------------------------------------------------------------------
 
 # unit roundoff of binary32 (24-bit significand, round to nearest): 2^-24
