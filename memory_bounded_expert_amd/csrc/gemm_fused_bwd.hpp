@@ -326,7 +326,7 @@ __attribute__((amdgpu_waves_per_eu(S::WGM * S::WGN / 4))) void fused_bwd_kernel(
           const float v0 = acc[0][i][j][q], v1 = acc[1][i][j][q];
           va[q] = f2bf(v0);
           vu[q] = f2bf(v1);
-          vh[q] = f2bf(__fdividef(v0, 1.f + __expf(-v0)) * v1);
+          vh[q] = f2bf(swiglu_h(v0, v1));
         }
         pa[i][j][0] = (uint32_t)va[0] | ((uint32_t)va[1] << 16);
         pa[i][j][1] = (uint32_t)va[2] | ((uint32_t)va[3] << 16);

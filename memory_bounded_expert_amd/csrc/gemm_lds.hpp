@@ -1077,7 +1077,7 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
     } else {
       stage_store(static_cast<T*>(p.C), [&](int i, int j, int q) {
         const float v0 = acc[0][i][j][q], v1 = acc[NB - 1][i][j][q];
-        return f2bf(__fdividef(v0, 1.f + __expf(-v0)) * v1);
+        return f2bf(swiglu_h(v0, v1));
       });
       if constexpr (EPI == Epi::SwiGLUSave) {
         stage_store(static_cast<T*>(p.C2), [&](int i, int j, int q) { return f2bf(acc[0][i][j][q]); });
@@ -1103,7 +1103,7 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
           static_cast<T*>(p.C)[o] = f2bf(v0);
         } else if constexpr (EPI == Epi::SwiGLU || EPI == Epi::SwiGLUSave) {
           const float v1 = acc[NB - 1][i][j][q];
-          const float hv = __fdividef(v0, 1.f + __expf(-v0)) * v1;
+          const float hv = swiglu_h(v0, v1);
           static_cast<T*>(p.C)[o] = f2bf(hv);
           if constexpr (EPI == Epi::SwiGLUSave) {
             static_cast<T*>(p.C2)[o] = f2bf(v0);
