@@ -22,11 +22,11 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
-// h = silu(a) u = a u / (1 + e^-a), the reciprocal by the hardware
-// instruction (about 1 ulp; h is rounded to bf16 right after)
-__device__ __forceinline__ float swiglu_h(float a, float u) {
-  return a * __builtin_amdgcn_rcpf(1.f + __expf(-a)) * u;
-}
+// The logistic 1 / (1 + e^-a), the reciprocal by the hardware instruction
+// (about 1 ulp; every bf16 value formed from it is rounded right after)
+__device__ __forceinline__ float logistic(float a) { return __builtin_amdgcn_rcpf(1.f + __expf(-a)); }
+// h = silu(a) u = a u / (1 + e^-a)
+__device__ __forceinline__ float swiglu_h(float a, float u) { return a * logistic(a) * u; }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -503,7 +503,7 @@ __attribute__((amdgpu_waves_per_eu(S::WGM * S::WGN / 4))) void fused_bwd_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float av = unpk(pa[i][j], q), uv = unpk(pu[i][j], q);
-          const float sa = 1.f / (1.f + expf(-av));
+          const float sa = logistic(av);
           const float d = rg[i][q] * acc2[i][j][q];
           const float v = o == 0 ? d * uv * sa * (1.f + av * (1.f - sa)) : d * av * sa;
           stg[(wm * WM + i * 16 + 4 * eg + q) * LD + wn * WN + j * 16 + e16] = f2bf(v);

@@ -961,7 +961,7 @@ __device__ __forceinline__ void gemm_lds_body(const Params& p, int bid) {
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
             part = fmaf(dv[q], hv[q], part);
-            const float sa = 1.f / (1.f + expf(-av[q]));
+            const float sa = logistic(av[q]);
             const float d = g * dv[q];
             da[q] = d * uv[q] * sa * (1.f + av[q] * (1.f - sa));
             du[q] = d * av[q] * sa;
